@@ -1,0 +1,277 @@
+// C ABI layer: host-side argument checks, workspace sizing, dispatch.
+// Every check runs before the first HIP call, so a rejected call enqueues
+// nothing and writes nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "prism_internal.h"
+
+namespace prism {
+
+static thread_local char g_err[512] = "";
+
+prism_status fail(prism_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+prism_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(PRISM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return PRISM_OK;
+}
+
+static bool dtype_ok(int dtype) {
+  return dtype == PRISM_FP32 || dtype == PRISM_BF16;
+}
+
+static prism_status make_geom(int T, int H, int W, int zt, int zh, int zw,
+                              ZoneGeom* g) {
+  PRISM_CHECK(T >= 1 && H >= 1 && W >= 1, PRISM_ERR_INVALID_ARG,
+              "grid extents must be >= 1 (T=%d H=%d W=%d)", T, H, W);
+  PRISM_CHECK(zt >= 1 && zh >= 1 && zw >= 1, PRISM_ERR_INVALID_ARG,
+              "zone extents must be >= 1 (%d,%d,%d)", zt, zh, zw);
+  PRISM_CHECK(zt <= 8 && zh <= 8 && zw <= 8, PRISM_ERR_UNSUPPORTED,
+              "zone extents above 8 are not supported (%d,%d,%d)", zt, zh,
+              zw);
+  PRISM_CHECK((long long)T * H * W <= (1LL << 30), PRISM_ERR_UNSUPPORTED,
+              "grid too large");
+  PRISM_CHECK(((long long)T * H * W) % PRISM_BLOCK_TOKENS == 0,
+              PRISM_ERR_SHAPE, "token count T*H*W=%lld is not a multiple of 64",
+              (long long)T * H * W);
+  g->T = T; g->H = H; g->W = W;
+  g->zt = zt; g->zh = zh; g->zw = zw;
+  g->nzt = ceil_div(T, zt); g->nzh = ceil_div(H, zh); g->nzw = ceil_div(W, zw);
+  g->nZ = g->nzt * g->nzh * g->nzw;
+  return PRISM_OK;
+}
+
+// Every zone extent kind (full or remainder along each axis) must admit the
+// requested shape (fixed) or at least one shape (dynamic).
+static prism_status check_zone_kinds(const ZoneGeom& g, int fixed_shape) {
+  int lt[2] = {g.zt, g.T % g.zt ? g.T % g.zt : g.zt};
+  int lh[2] = {g.zh, g.H % g.zh ? g.H % g.zh : g.zh};
+  int lw[2] = {g.zw, g.W % g.zw ? g.W % g.zw : g.zw};
+  if (g.T < g.zt) lt[0] = lt[1] = g.T;
+  if (g.H < g.zh) lh[0] = lh[1] = g.H;
+  if (g.W < g.zw) lw[0] = lw[1] = g.W;
+  for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 2; ++b)
+      for (int c = 0; c < 2; ++c) {
+        int Lt = lt[a], Lh = lh[b], Lw = lw[c];
+        if (fixed_shape >= 0) {
+          PRISM_CHECK(shape_fits(fixed_shape, Lt, Lh, Lw), PRISM_ERR_SHAPE,
+                      "shape %d does not fit zone %dx%dx%d", fixed_shape, Lt,
+                      Lh, Lw);
+        } else {
+          bool any = false;
+          for (int s = 0; s < kNumShapes; ++s) any |= shape_fits(s, Lt, Lh, Lw);
+          PRISM_CHECK(any, PRISM_ERR_SHAPE,
+                      "no candidate shape fits zone %dx%dx%d", Lt, Lh, Lw);
+        }
+      }
+  return PRISM_OK;
+}
+
+static prism_status check_heads(int B, int Hh, int N, int d) {
+  PRISM_CHECK(B >= 1 && Hh >= 1 && N >= 1 && d >= 1, PRISM_ERR_INVALID_ARG,
+              "sizes must be >= 1 (B=%d Hh=%d N=%d d=%d)", B, Hh, N, d);
+  PRISM_CHECK(N % PRISM_BLOCK_TOKENS == 0, PRISM_ERR_SHAPE,
+              "N=%d is not a multiple of 64", N);
+  PRISM_CHECK(d == 64 || d == 128, PRISM_ERR_UNSUPPORTED,
+              "head_dim %d not built (64 or 128)", d);
+  PRISM_CHECK((long long)B * Hh * N * d < (1LL << 40), PRISM_ERR_UNSUPPORTED,
+              "tensor too large");
+  return PRISM_OK;
+}
+
+}  // namespace prism
+
+using namespace prism;
+
+extern "C" {
+
+const char* prism_last_error(void) { return g_err; }
+
+int prism_version(void) { return 100; }
+
+int prism_shape_table(int32_t* out_thw) {
+  if (!out_thw) return kNumShapes;
+  for (int s = 0; s < kNumShapes; ++s) {
+    Shape sh = shape_of(s);
+    out_thw[3 * s + 0] = sh.t;
+    out_thw[3 * s + 1] = sh.h;
+    out_thw[3 * s + 2] = sh.w;
+  }
+  return kNumShapes;
+}
+
+size_t prism_zone_shapes_workspace_bytes(int B, int T, int H, int W, int C,
+                                         int zone_t, int zone_h, int zone_w) {
+  ZoneGeom g;
+  if (B < 1 || C < 1 || make_geom(T, H, W, zone_t, zone_h, zone_w, &g) != PRISM_OK)
+    return 0;
+  return zone_shapes_ws_bytes(B, g, C);
+}
+
+prism_status prism_zone_shapes(const void* feat, const void* a2v_res,
+                               int dtype, int B, int T, int H, int W, int C,
+                               int zone_t, int zone_h, int zone_w,
+                               double lambda_a2v, int fixed_shape,
+                               int32_t* zone_shape, int32_t* perm,
+                               int32_t* inv_perm, double* zone_stats,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  clear_error();
+  ZoneGeom g;
+  prism_status st = make_geom(T, H, W, zone_t, zone_h, zone_w, &g);
+  if (st != PRISM_OK) return st;
+  PRISM_CHECK(B >= 1, PRISM_ERR_INVALID_ARG, "B=%d must be >= 1", B);
+  PRISM_CHECK(fixed_shape >= -1 && fixed_shape < kNumShapes,
+              PRISM_ERR_INVALID_ARG, "fixed_shape=%d outside [-1, 12]",
+              fixed_shape);
+  PRISM_CHECK(zone_shape && perm, PRISM_ERR_INVALID_ARG,
+              "zone_shape and perm must not be NULL");
+  st = check_zone_kinds(g, fixed_shape);
+  if (st != PRISM_OK) return st;
+  if (fixed_shape < 0) {
+    PRISM_CHECK(feat != nullptr, PRISM_ERR_INVALID_ARG,
+                "feat must not be NULL when shapes are chosen per zone");
+    PRISM_CHECK(C >= 1, PRISM_ERR_INVALID_ARG, "C=%d must be >= 1", C);
+    PRISM_CHECK(dtype_ok(dtype), PRISM_ERR_INVALID_ARG, "bad dtype %d", dtype);
+    PRISM_CHECK(C % 8 == 0, PRISM_ERR_UNSUPPORTED,
+                "C=%d must be a multiple of 8", C);
+    PRISM_CHECK(isfinite(lambda_a2v) && lambda_a2v >= 0.0,
+                PRISM_ERR_INVALID_ARG, "lambda_a2v must be finite and >= 0");
+    PRISM_CHECK((long long)B * T * H * W * C < (1LL << 40),
+                PRISM_ERR_UNSUPPORTED, "feature tensor too large");
+    size_t need = zone_shapes_ws_bytes(B, g, C);
+    PRISM_CHECK(workspace != nullptr && workspace_bytes >= need,
+                PRISM_ERR_WORKSPACE,
+                "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  }
+  return launch_zone_shapes(feat, a2v_res, dtype, B, g, C, lambda_a2v,
+                            fixed_shape, zone_shape, perm, inv_perm,
+                            zone_stats, workspace, (hipStream_t)stream);
+}
+
+prism_status prism_pool_blocks(const void* q, const void* k, int dtype,
+                               const int32_t* perm, int B, int Hh, int N,
+                               int d, double* q_mean, double* k_mean,
+                               double* proxy, void* stream) {
+  clear_error();
+  prism_status st = check_heads(B, Hh, N, d);
+  if (st != PRISM_OK) return st;
+  PRISM_CHECK(dtype_ok(dtype), PRISM_ERR_INVALID_ARG, "bad dtype %d", dtype);
+  PRISM_CHECK(q && k && perm && q_mean && k_mean && proxy,
+              PRISM_ERR_INVALID_ARG, "null pointer argument");
+  const int Nb = N / PRISM_BLOCK_TOKENS;
+  PRISM_CHECK(Nb <= 8192, PRISM_ERR_UNSUPPORTED, "Nb=%d above 8192", Nb);
+  return launch_pool_proxy(q, k, dtype, perm, B, Hh, N, d, q_mean, k_mean,
+                           proxy, (hipStream_t)stream);
+}
+
+prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
+                                 int top_k, double cdf_threshold,
+                                 int32_t* counts, int32_t* kv_idx,
+                                 int capacity, void* stream) {
+  clear_error();
+  PRISM_CHECK(B >= 1 && Hh >= 1 && Nb >= 1, PRISM_ERR_INVALID_ARG,
+              "sizes must be >= 1 (B=%d Hh=%d Nb=%d)", B, Hh, Nb);
+  PRISM_CHECK(proxy && counts && kv_idx, PRISM_ERR_INVALID_ARG,
+              "null pointer argument");
+  PRISM_CHECK(top_k >= 0, PRISM_ERR_INVALID_ARG, "top_k=%d must be >= 0",
+              top_k);
+  PRISM_CHECK(cdf_threshold >= 0.0 && cdf_threshold <= 1.0,
+              PRISM_ERR_INVALID_ARG, "cdf_threshold=%g outside [0, 1]",
+              cdf_threshold);
+  PRISM_CHECK(capacity >= Nb, PRISM_ERR_SHAPE, "capacity=%d < Nb=%d",
+              capacity, Nb);
+  PRISM_CHECK(Nb <= 8192, PRISM_ERR_UNSUPPORTED, "Nb=%d above 8192", Nb);
+  return launch_select(proxy, B, Hh, Nb, top_k, cdf_threshold, counts, kv_idx,
+                       capacity, (hipStream_t)stream);
+}
+
+size_t prism_sparse_attn_fwd_workspace_bytes(int B, int Hh, int N, int d) {
+  (void)B; (void)Hh; (void)N; (void)d;
+  return 0;
+}
+
+static prism_status check_attn_common(const void* q, const void* k,
+                                      const void* v, int dtype,
+                                      const int32_t* perm,
+                                      const int32_t* counts,
+                                      const int32_t* kv_idx, int capacity,
+                                      int B, int Hh, int N, int d,
+                                      float softmax_scale) {
+  prism_status st = check_heads(B, Hh, N, d);
+  if (st != PRISM_OK) return st;
+  PRISM_CHECK(dtype_ok(dtype), PRISM_ERR_INVALID_ARG, "bad dtype %d", dtype);
+  PRISM_CHECK(q && k && v && perm && counts && kv_idx, PRISM_ERR_INVALID_ARG,
+              "null pointer argument");
+  PRISM_CHECK(capacity >= N / PRISM_BLOCK_TOKENS, PRISM_ERR_SHAPE,
+              "capacity=%d < Nb=%d", capacity, N / PRISM_BLOCK_TOKENS);
+  PRISM_CHECK(isfinite(softmax_scale), PRISM_ERR_INVALID_ARG,
+              "softmax_scale must be finite");
+  return PRISM_OK;
+}
+
+prism_status prism_sparse_attn_fwd(const void* q, const void* k,
+                                   const void* v, int dtype,
+                                   const int32_t* perm, const int32_t* counts,
+                                   const int32_t* kv_idx, int capacity, int B,
+                                   int Hh, int N, int d, float softmax_scale,
+                                   void* o, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  clear_error();
+  (void)workspace; (void)workspace_bytes;
+  prism_status st = check_attn_common(q, k, v, dtype, perm, counts, kv_idx,
+                                      capacity, B, Hh, N, d, softmax_scale);
+  if (st != PRISM_OK) return st;
+  PRISM_CHECK(o && lse, PRISM_ERR_INVALID_ARG, "null output pointer");
+  float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+  return launch_attn_fwd(q, k, v, dtype, perm, counts, kv_idx, capacity, B,
+                         Hh, N, d, scale, o, lse, (hipStream_t)stream);
+}
+
+size_t prism_sparse_attn_bwd_workspace_bytes(int B, int Hh, int N, int d) {
+  if (check_heads(B, Hh, N, d) != PRISM_OK) return 0;
+  return attn_bwd_ws_bytes(B, Hh, N, d);
+}
+
+prism_status prism_sparse_attn_bwd(const void* q, const void* k,
+                                   const void* v, const void* o,
+                                   const void* d_o, const float* lse,
+                                   int dtype, const int32_t* perm,
+                                   const int32_t* counts,
+                                   const int32_t* kv_idx, int capacity, int B,
+                                   int Hh, int N, int d, float softmax_scale,
+                                   float* dq, float* dk, float* dv,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  clear_error();
+  prism_status st = check_attn_common(q, k, v, dtype, perm, counts, kv_idx,
+                                      capacity, B, Hh, N, d, softmax_scale);
+  if (st != PRISM_OK) return st;
+  PRISM_CHECK(o && d_o && lse && dq && dk && dv, PRISM_ERR_INVALID_ARG,
+              "null pointer argument");
+  size_t need = attn_bwd_ws_bytes(B, Hh, N, d);
+  PRISM_CHECK(workspace != nullptr && workspace_bytes >= need,
+              PRISM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+              need, workspace ? workspace_bytes : (size_t)0);
+  float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+  return launch_attn_bwd(q, k, v, o, d_o, lse, dtype, perm, counts, kv_idx,
+                         capacity, B, Hh, N, d, scale, dq, dk, dv, workspace,
+                         (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Internal helpers shared by the gfx950 kernels and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/prism.h"
+
+namespace prism {
+
+// ------------------------------------------------------------------ errors
+prism_status fail(prism_status st, const char* fmt, ...);
+void clear_error();
+// Wraps the launch status of the most recent kernel.
+prism_status check_launch(const char* what);
+
+#define PRISM_CHECK(cond, st, ...)            \
+  do {                                        \
+    if (!(cond)) return prism::fail(st, __VA_ARGS__); \
+  } while (0)
+
+// ------------------------------------------------------------ shape table
+struct Shape { int t, h, w; };
+constexpr int kNumShapes = 13;
+// (t, h, w) per id; see prism_shape_table() in include/prism.h.
+__host__ __device__ inline Shape shape_of(int id) {
+  constexpr int tbl[kNumShapes][3] = {
+      {4, 4, 4}, {2, 4, 8}, {2, 8, 4}, {4, 2, 8}, {4, 8, 2}, {8, 2, 4},
+      {8, 4, 2}, {1, 8, 8}, {8, 1, 8}, {8, 8, 1}, {2, 2, 16}, {2, 16, 2},
+      {16, 2, 2}};
+  return Shape{tbl[id][0], tbl[id][1], tbl[id][2]};
+}
+__host__ __device__ inline bool shape_fits(int id, int Lt, int Lh, int Lw) {
+  Shape s = shape_of(id);
+  return Lt % s.t == 0 && Lh % s.h == 0 && Lw % s.w == 0;
+}
+
+// ------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// round to nearest even; NaN stays NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------- stage launchers
+struct ZoneGeom {
+  int T, H, W, zt, zh, zw, nzt, nzh, nzw, nZ;
+};
+prism_status launch_zone_shapes(const void* feat, const void* a2v, int dtype,
+                                int B, const ZoneGeom& g, int C, double lam,
+                                int fixed_shape, int32_t* zone_shape,
+                                int32_t* perm, int32_t* inv_perm,
+                                double* zone_stats, void* ws,
+                                hipStream_t stream);
+size_t zone_shapes_ws_bytes(int B, const ZoneGeom& g, int C);
+
+prism_status launch_pool_proxy(const void* q, const void* k, int dtype,
+                               const int32_t* perm, int B, int Hh, int N,
+                               int d, double* q_mean, double* k_mean,
+                               double* proxy, hipStream_t stream);
+
+prism_status launch_select(const double* proxy, int B, int Hh, int Nb,
+                           int top_k, double tau, int32_t* counts,
+                           int32_t* kv_idx, int capacity, hipStream_t stream);
+
+prism_status launch_attn_fwd(const void* q, const void* k, const void* v,
+                             int dtype, const int32_t* perm,
+                             const int32_t* counts, const int32_t* kv_idx,
+                             int capacity, int B, int Hh, int N, int d,
+                             float scale, void* o, float* lse,
+                             hipStream_t stream);
+
+size_t attn_bwd_ws_bytes(int B, int Hh, int N, int d);
+prism_status launch_attn_bwd(const void* q, const void* k, const void* v,
+                             const void* o, const void* d_o, const float* lse,
+                             int dtype, const int32_t* perm,
+                             const int32_t* counts, const int32_t* kv_idx,
+                             int capacity, int B, int Hh, int N, int d,
+                             float scale, float* dq, float* dk, float* dv,
+                             void* ws, hipStream_t stream);
+
+}  // namespace prism

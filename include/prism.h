@@ -1,0 +1,199 @@
+/*
+ * prism.h -- C ABI of the MI355X (gfx950) dynamic block-shape, block-sparse
+ * video self-attention library (libprism.so).
+ *
+ * The method (Prism): the T x H x W video token grid is split into
+ * spatiotemporal macro-zones; every zone picks one of 13 block shapes of 64
+ * tokens from its directional feature variance plus the audio-to-video
+ * residual norm; tokens are grouped into those blocks; queries and keys are
+ * mean-pooled per block into a block proxy score; every query block keeps
+ * its top-k KV blocks plus more in descending score order until the
+ * cumulative proxy mass reaches cdf_threshold; attention then runs over the
+ * kept blocks only.  Sources: "Tencent-Hunyuan/Prism" README, section
+ * "Overview"; the Prism architecture walk-through (wmrh.cn), sections
+ * "一个巧妙的联动：桥接残差反哺稀疏注意力" and
+ * "三者如何协同：一步去噪里发生了什么"; the "Prism: Dynamic Sparse
+ * Attention for Native 2K Joint Video-Audio Generation Model Training"
+ * abstract page (block proxy scores, cumulative-mass selection, online
+ * softmax over selected blocks).
+ *
+ * Conventions shared by every call
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or keeps them; scratch memory comes in through
+ *    `workspace` (size from the matching *_workspace_bytes query).
+ *  - Every argument is checked on the host before any HIP call.  On a
+ *    failed check nothing is written or enqueued and a non-zero status is
+ *    returned; prism_last_error() gives a message (thread-local).
+ *  - Work is only enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream); results are valid once the caller synchronises that stream.
+ *    The library never synchronises.
+ *  - Token layout is raster order t*H*W + h*W + w.  Per-head tensors are
+ *    [B, Hh, N, d] contiguous; block-ordered data is reached through `perm`
+ *    (the caller never permutes tensors).
+ *  - Blocks always hold 64 tokens, so Nb = N / 64.
+ *  - Calls that share a workspace or outputs must not overlap in time.
+ */
+#ifndef PRISM_H
+#define PRISM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PRISM_OK = 0,
+  PRISM_ERR_INVALID_ARG = 1, /* null pointer, size < 1, bad dtype, k < 0, ... */
+  PRISM_ERR_SHAPE = 2,       /* inconsistent sizes, zone without a legal shape */
+  PRISM_ERR_UNSUPPORTED = 3, /* head_dim / dtype combination not built        */
+  PRISM_ERR_WORKSPACE = 4,   /* workspace missing or too small                */
+  PRISM_ERR_HIP = 5          /* a HIP launch or API call failed               */
+} prism_status;
+
+typedef enum { PRISM_FP32 = 0, PRISM_BF16 = 1 } prism_dtype;
+
+#define PRISM_BLOCK_TOKENS 64
+#define PRISM_NUM_SHAPES 13
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* prism_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int prism_version(void);
+
+/* The 13 candidate block shapes as (t, h, w) triples, written to
+ * out_thw[3*id + {0,1,2}] (host memory, 39 ints).  Returns 13.  The pages
+ * name (4,4,4), (8,2,4) and (2,4,8); the table holds every power-of-two
+ * 64-token box whose longest side is at most 8x its shortest. */
+int prism_shape_table(int32_t* out_thw);
+
+/* ---------------------------------------------------------------------
+ * Stage 1 -- zone shapes and token permutation.
+ * README "Overview" and walk-through "三者如何协同": for each macro-zone the
+ * directional variance v_a of the video features (per channel, along lines
+ * parallel to axis a in {T, H, W}, averaged over lines and channels) and
+ * the directional variance u_a of the per-token a2v residual RMS norm
+ * ||dh||_2 / sqrt(C) combine as w_a = v_a + lambda_a2v * u_a; the zone takes
+ * the legal shape (each extent divides the zone extent) minimising
+ * sum_a w_a (e_a^2 - 1) / (L_a^2 - 1), lowest id on ties.
+ *
+ * feat, a2v_res : [B, N, C] raster tokens, dtype; a2v_res may be NULL (no
+ *                 audio term).  Both may be NULL when fixed_shape >= 0.
+ * zone_t/h/w    : macro-zone extents (8, 8, 8 in the pages' setting); zones
+ *                 tile the grid from the origin, the last zone along an
+ *                 axis keeps the remainder.  nZ = ceil(T/zt)*ceil(H/zh)*
+ *                 ceil(W/zw).
+ * fixed_shape   : -1 = choose per zone; 0..12 = force that shape everywhere.
+ * zone_shape    : out [B, nZ] int32 shape ids (zones in raster order).
+ * perm          : out [B, N] int32; perm[b][64*i + r] = raster token index of
+ *                 the r-th token of block i.  Blocks are numbered zone-major,
+ *                 the block lattice of a zone in raster order, tokens inside a
+ *                 block in raster order.
+ * inv_perm      : out [B, N] int32 (slot of each raster token) or NULL.
+ * zone_stats    : out [B, nZ, 6] fp64 (v_T, v_H, v_W, u_T, u_H, u_W) or NULL.
+ * Errors: SHAPE if N % 64 != 0, a zone has no legal shape, or fixed_shape
+ * does not fit every zone; WORKSPACE if workspace_bytes is below
+ * prism_zone_shapes_workspace_bytes(). */
+size_t prism_zone_shapes_workspace_bytes(int B, int T, int H, int W, int C,
+                                         int zone_t, int zone_h, int zone_w);
+prism_status prism_zone_shapes(const void* feat, const void* a2v_res,
+                               int dtype, int B, int T, int H, int W, int C,
+                               int zone_t, int zone_h, int zone_w,
+                               double lambda_a2v, int fixed_shape,
+                               int32_t* zone_shape, int32_t* perm,
+                               int32_t* inv_perm, double* zone_stats,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* ---------------------------------------------------------------------
+ * Stage 2 -- block mean-pooling and block proxy scores.
+ * README "Overview" (block-level features) and the abstract page (block
+ * proxy scores): qbar_i = mean of the 64 query rows of block i (kbar
+ * likewise), accumulated in fp64; proxy[i][j] = softmax over j of
+ * <qbar_i, kbar_j> / sqrt(d), over all Nb blocks of the same (b, h), fp64.
+ *
+ * q, k   : [B, Hh, N, d] dtype.  perm: [B, N] from stage 1.
+ * q_mean, k_mean : out [B, Hh, Nb, d] fp64.
+ * proxy  : out [B, Hh, Nb, Nb] fp64, rows sum to 1.
+ * d must be 64 or 128. */
+prism_status prism_pool_blocks(const void* q, const void* k, int dtype,
+                               const int32_t* perm, int B, int Hh, int N,
+                               int d, double* q_mean, double* k_mean,
+                               double* proxy, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Stage 3 -- hybrid top-k + top-p block selection.
+ * Walk-through "三者如何协同": keep the top_k highest-scoring KV blocks, then
+ * keep adding blocks in descending proxy order until the cumulative proxy
+ * mass reaches cdf_threshold (default 0.20).  Order: descending score,
+ * equal scores by lower block index.  The mass is the running fp64 sum in
+ * that order; "reaches" means >=.  At least one block is kept; top_k is
+ * clipped to Nb.  Count c = min(Nb, max(top_k, m*)), m* the first prefix
+ * length whose mass reaches the threshold.
+ *
+ * proxy    : [B, Hh, Nb, Nb] fp64 (non-negative rows).
+ * counts   : out [B, Hh, Nb] int32.
+ * kv_idx   : out [B, Hh, Nb, capacity] int32, the first counts[...] entries
+ *            of each row hold the kept block ids in ascending order; the
+ *            rest of the row is not written.  capacity >= Nb.
+ * Nb must be at most 8192.
+ * Errors: INVALID_ARG if top_k < 0 or cdf_threshold is not in [0, 1]. */
+prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
+                                 int top_k, double cdf_threshold,
+                                 int32_t* counts, int32_t* kv_idx,
+                                 int capacity, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Stage 4 -- block-sparse attention, forward.
+ * Abstract page (sparse computation over the selected KV blocks with online
+ * softmax) and README "Overview": for each query block i and each of its 64
+ * query rows, exact softmax attention over the 64 * counts[i] keys of the
+ * listed blocks; no causal mask, no dropout.
+ *
+ * q, k, v : [B, Hh, N, d] dtype (bf16: MFMA path with fp32 accumulation;
+ *           fp32: reference-precision path).
+ * perm, counts, kv_idx, capacity : from stages 1 and 3.  Every count must be
+ *           in [1, Nb] and every listed id in [0, Nb) (caller's contract).
+ * softmax_scale : <= 0 means 1/sqrt(d).
+ * o   : out [B, Hh, N, d] dtype, raster order.
+ * lse : out [B, Hh, N] fp32, natural-log logsumexp of the scaled scores.
+ * workspace: may be NULL (none needed; kept for future split-KV work). */
+size_t prism_sparse_attn_fwd_workspace_bytes(int B, int Hh, int N, int d);
+prism_status prism_sparse_attn_fwd(const void* q, const void* k,
+                                   const void* v, int dtype,
+                                   const int32_t* perm, const int32_t* counts,
+                                   const int32_t* kv_idx, int capacity, int B,
+                                   int Hh, int N, int d, float softmax_scale,
+                                   void* o, float* lse, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Stage 4 -- block-sparse attention, backward (training).
+ * README "Overview": the method trains with the sparse attention, so the
+ * gradient runs over the same kept blocks.  The selection is constant (no
+ * gradient through routing).  With P = exp(s - lse) and D_r = <dO_r, O_r>:
+ * dV = P^T dO, dS = P * (dO V^T - D), dQ = dS K * scale, dK = dS^T Q * scale.
+ *
+ * q, k, v, o, d_o : [B, Hh, N, d] dtype; lse [B, Hh, N] fp32 from the
+ *                   forward.
+ * dq, dk, dv      : out [B, Hh, N, d] fp32, raster order (fully written).
+ * workspace       : at least prism_sparse_attn_bwd_workspace_bytes(). */
+size_t prism_sparse_attn_bwd_workspace_bytes(int B, int Hh, int N, int d);
+prism_status prism_sparse_attn_bwd(const void* q, const void* k,
+                                   const void* v, const void* o,
+                                   const void* d_o, const float* lse,
+                                   int dtype, const int32_t* perm,
+                                   const int32_t* counts,
+                                   const int32_t* kv_idx, int capacity, int B,
+                                   int Hh, int N, int d, float softmax_scale,
+                                   float* dq, float* dk, float* dv,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRISM_H */

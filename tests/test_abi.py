@@ -1,0 +1,126 @@
+"""The C ABI library loads, exports every declared entry point, and rejects
+invalid arguments on the host before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_block_sparse_shape_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prism.h")
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(prism_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = P.lib()
+    names = _declared()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(L, n), n
+    # the Python binding carries the same names
+    for n in names:
+        assert hasattr(P, n), n
+
+
+def test_shape_table():
+    tbl = P.shape_table()
+    assert len(tbl) == 13
+    assert tbl[0] == (4, 4, 4) and (8, 2, 4) in tbl and (2, 4, 8) in tbl
+    assert all(t * h * w == 64 for t, h, w in tbl)
+    assert P.lib().prism_shape_table(None) == 13
+    assert P.prism_version() >= 100
+
+
+def test_workspace_queries():
+    n = P.prism_zone_shapes_workspace_bytes(1, 20, 90, 160, 3072, 8, 8, 8)
+    # 720 zones x 96 fp32 slices x 3 doubles + one double per token
+    assert n >= 720 * 96 * 3 * 8 + 288000 * 8
+    assert P.prism_zone_shapes_workspace_bytes(1, 20, 90, 161, 3072, 8, 8, 8) == 0
+    nb = 4500
+    m = P.prism_sparse_attn_bwd_workspace_bytes(1, 24, 288000, 128)
+    assert m >= 24 * 288000 * 4 + 24 * nb * ((nb + 31) // 32) * 4
+    assert P.prism_sparse_attn_bwd_workspace_bytes(1, 24, 288000, 96) == 0
+    assert P.prism_sparse_attn_fwd_workspace_bytes(1, 24, 288000, 128) == 0
+
+
+def _expect(status, fn, *args, **kw):
+    with pytest.raises(P.PrismError) as ei:
+        fn(*args, **kw)
+    assert ei.value.status == status, str(ei.value)
+    assert P.prism_last_error() != ""
+
+
+def test_zone_shapes_rejections():
+    zs = dict(feat=FAKE, a2v_res=FAKE, dtype=1, B=1, T=20, H=68, W=120, C=3072,
+              zone_t=8, zone_h=8, zone_w=8, lambda_a2v=1.0, fixed_shape=-1,
+              zone_shape=FAKE, perm=FAKE, inv_perm=None, zone_stats=None,
+              workspace=FAKE, workspace_bytes=1 << 40, stream=None)
+
+    def call(**kw):
+        a = dict(zs)
+        a.update(kw)
+        return P.prism_zone_shapes(*a.values())
+
+    _expect(2, call, W=121)                       # N % 64 != 0
+    _expect(1, call, feat=None)                   # dynamic needs features
+    _expect(1, call, perm=None)
+    _expect(1, call, dtype=7)
+    _expect(1, call, B=0)
+    _expect(1, call, fixed_shape=13)
+    _expect(2, call, fixed_shape=5, T=20)         # (8,2,4) vs T-remainder 4
+    _expect(3, call, zone_t=16)
+    _expect(3, call, C=3070)
+    _expect(4, call, workspace_bytes=16)
+    _expect(4, call, workspace=None)
+    _expect(1, call, lambda_a2v=-1.0)
+    # a grid whose remainder zone admits no shape: 4 x 1 x 8 remainder
+    _expect(2, call, T=4, H=9, W=64, fixed_shape=-1)
+
+
+def test_pool_select_rejections():
+    _expect(3, P.prism_pool_blocks, FAKE, FAKE, 1, FAKE, 1, 2, 256, 96, FAKE,
+            FAKE, FAKE, None)
+    _expect(2, P.prism_pool_blocks, FAKE, FAKE, 1, FAKE, 1, 2, 250, 64, FAKE,
+            FAKE, FAKE, None)
+    _expect(1, P.prism_pool_blocks, None, FAKE, 1, FAKE, 1, 2, 256, 64, FAKE,
+            FAKE, FAKE, None)
+    _expect(3, P.prism_pool_blocks, FAKE, FAKE, 1, FAKE, 1, 1, 64 * 8193, 64,
+            FAKE, FAKE, FAKE, None)
+    _expect(1, P.prism_select_blocks, FAKE, 1, 2, 4, -1, 0.2, FAKE, FAKE, 4,
+            None)
+    _expect(1, P.prism_select_blocks, FAKE, 1, 2, 4, 1, 1.5, FAKE, FAKE, 4,
+            None)
+    _expect(1, P.prism_select_blocks, FAKE, 1, 2, 4, 1, float("nan"), FAKE,
+            FAKE, 4, None)
+    _expect(2, P.prism_select_blocks, FAKE, 1, 2, 4, 1, 0.2, FAKE, FAKE, 3,
+            None)
+    _expect(3, P.prism_select_blocks, FAKE, 1, 1, 8193, 1, 0.2, FAKE, FAKE,
+            8193, None)
+    _expect(1, P.prism_select_blocks, FAKE, 1, 2, 4, 1, 0.2, None, FAKE, 4,
+            None)
+
+
+def test_attention_rejections():
+    base = [FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 4, 1, 2, 256, 128, -1.0,
+            FAKE, FAKE, None, 0, None]
+    _expect(3, P.prism_sparse_attn_fwd, *(base[:11] + [80] + base[12:]))
+    _expect(2, P.prism_sparse_attn_fwd, *(base[:7] + [3] + base[8:]))
+    _expect(1, P.prism_sparse_attn_fwd, *([None] + base[1:]))
+    _expect(1, P.prism_sparse_attn_fwd, *(base[:13] + [None] + base[14:]))
+    _expect(1, P.prism_sparse_attn_fwd, *(base[:3] + [2] + base[4:]))
+    _expect(1, P.prism_sparse_attn_fwd, *(base[:12] + [float("inf")] + base[13:]))
+    bwd = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 4, 1, 2,
+           256, 128, -1.0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    _expect(4, P.prism_sparse_attn_bwd, *(bwd[:20] + [8] + bwd[21:]))
+    _expect(4, P.prism_sparse_attn_bwd, *(bwd[:19] + [None] + bwd[20:]))
+    _expect(1, P.prism_sparse_attn_bwd, *(bwd[:4] + [None] + bwd[5:]))
+    _expect(3, P.prism_sparse_attn_bwd, *(bwd[:14] + [32] + bwd[15:]))
