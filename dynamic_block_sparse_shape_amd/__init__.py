@@ -24,7 +24,9 @@ __all__ = [
     "prism_sparse_attn_fwd", "prism_sparse_attn_bwd",
     "prism_zone_shapes_workspace_bytes", "prism_sparse_attn_bwd_workspace_bytes",
     "prism_sparse_attn_fwd_workspace_bytes", "prism_shape_table",
-    "prism_last_error", "prism_version",
+    "prism_last_error", "prism_version", "prism_profile_enable",
+    "prism_profile_reset", "prism_profile_count", "prism_profile_name",
+    "prism_profile_ms", "kernel_times",
     "zone_shapes", "pool_blocks", "select_blocks", "sparse_attn_fwd",
     "sparse_attn_bwd", "shape_table",
 ]
@@ -42,6 +44,11 @@ _c_int, _c_sz, _c_dbl, _c_flt, _c_p = (ctypes.c_int, ctypes.c_size_t,
 _SIGS = {
     "prism_last_error": (ctypes.c_char_p, []),
     "prism_version": (_c_int, []),
+    "prism_profile_enable": (_c_int, [_c_int]),
+    "prism_profile_reset": (None, []),
+    "prism_profile_count": (_c_int, []),
+    "prism_profile_name": (ctypes.c_char_p, [_c_int]),
+    "prism_profile_ms": (_c_flt, [_c_int]),
     "prism_shape_table": (_c_int, [_c_p]),
     "prism_zone_shapes_workspace_bytes": (_c_sz, [_c_int] * 8),
     "prism_zone_shapes": (_c_int, [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int,
@@ -104,6 +111,32 @@ def prism_last_error() -> str:
 
 def prism_version() -> int:
     return lib().prism_version()
+
+
+def prism_profile_enable(on: int) -> int:
+    return _call("prism_profile_enable", int(on))
+
+
+def prism_profile_reset() -> None:
+    lib().prism_profile_reset()
+
+
+def prism_profile_count() -> int:
+    return lib().prism_profile_count()
+
+
+def prism_profile_name(i: int) -> str:
+    return lib().prism_profile_name(i).decode()
+
+
+def prism_profile_ms(i: int) -> float:
+    return lib().prism_profile_ms(i)
+
+
+def kernel_times():
+    """[(kernel name, ms)] of the launches recorded since the last reset."""
+    return [(prism_profile_name(i), prism_profile_ms(i))
+            for i in range(prism_profile_count())]
 
 
 def prism_shape_table(out_ptr) -> int:

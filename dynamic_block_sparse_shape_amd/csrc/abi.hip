@@ -2,6 +2,7 @@
 // Every check runs before the first HIP call, so a rejected call enqueues
 // nothing and writes nothing.
 #include <math.h>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -27,6 +28,30 @@ prism_status check_launch(const char* what) {
   if (e != hipSuccess)
     return fail(PRISM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return PRISM_OK;
+}
+
+// ------------------------------------------------------ kernel timing
+namespace {
+constexpr int kProfMax = 4096;
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+int g_prof_dev = -1;
+int g_prof_n = 0;
+hipEvent_t g_prof_ev[kProfMax][2];
+const char* g_prof_name[kProfMax];
+}  // namespace
+
+ProfScope::ProfScope(hipStream_t s, const char* name) : slot(-1), stream(s) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on || g_prof_n >= kProfMax) return;
+  slot = g_prof_n++;
+  g_prof_name[slot] = name;
+  (void)hipEventRecord(g_prof_ev[slot][0], stream);
+}
+
+ProfScope::~ProfScope() {
+  if (slot >= 0) (void)hipEventRecord(g_prof_ev[slot][1], stream);
 }
 
 static bool dtype_ok(int dtype) {
@@ -102,6 +127,46 @@ extern "C" {
 const char* prism_last_error(void) { return g_err; }
 
 int prism_version(void) { return 100; }
+
+int prism_profile_enable(int on) {
+  clear_error();
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (on && !g_prof_on) {
+    if (g_prof_dev < 0) {
+      if (hipGetDevice(&g_prof_dev) != hipSuccess) {
+        g_prof_dev = -1;
+        return fail(PRISM_ERR_HIP, "hipGetDevice failed");
+      }
+      for (int i = 0; i < kProfMax; ++i)
+        for (int e = 0; e < 2; ++e)
+          if (hipEventCreate(&g_prof_ev[i][e]) != hipSuccess)
+            return fail(PRISM_ERR_HIP, "hipEventCreate failed");
+    }
+    g_prof_n = 0;
+  }
+  g_prof_on = on != 0;
+  return PRISM_OK;
+}
+
+void prism_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_n = 0;
+}
+
+int prism_profile_count(void) { return g_prof_n; }
+
+const char* prism_profile_name(int i) {
+  return (i >= 0 && i < g_prof_n) ? g_prof_name[i] : "";
+}
+
+float prism_profile_ms(int i) {
+  if (i < 0 || i >= g_prof_n) return -1.f;
+  if (hipEventSynchronize(g_prof_ev[i][1]) != hipSuccess) return -1.f;
+  float ms = -1.f;
+  if (hipEventElapsedTime(&ms, g_prof_ev[i][0], g_prof_ev[i][1]) != hipSuccess)
+    return -1.f;
+  return ms;
+}
 
 int prism_shape_table(int32_t* out_thw) {
   if (!out_thw) return kNumShapes;

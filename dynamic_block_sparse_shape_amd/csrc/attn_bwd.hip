@@ -468,39 +468,39 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
   const long long nbits = (long long)B * Hh * Nb * words;
 
   if (dtype == PRISM_BF16)
-    hipLaunchKernelGGL((bwd_delta<uint16_t, D>), dim3((unsigned)((rows + 15) / 16)),
+    PRISM_LAUNCH("bwd_delta", (bwd_delta<uint16_t, D>), dim3((unsigned)((rows + 15) / 16)),
                        dim3(256), 0, stream, (const uint16_t*)o, (const uint16_t*)d_o,
                        rows, delta);
   else
-    hipLaunchKernelGGL((bwd_delta<float, D>), dim3((unsigned)((rows + 15) / 16)),
+    PRISM_LAUNCH("bwd_delta", (bwd_delta<float, D>), dim3((unsigned)((rows + 15) / 16)),
                        dim3(256), 0, stream, (const float*)o, (const float*)d_o, rows,
                        delta);
   prism_status st = check_launch("bwd_delta");
   if (st != PRISM_OK) return st;
   const unsigned cg = (unsigned)std::min<long long>((nbits + 255) / 256, 65535);
-  hipLaunchKernelGGL(bitmap_clear, dim3(cg), dim3(256), 0, stream, bits, nbits);
+  PRISM_LAUNCH("bitmap_clear", bitmap_clear, dim3(cg), dim3(256), 0, stream, bits, nbits);
   if ((st = check_launch("bitmap_clear")) != PRISM_OK) return st;
   const long long qrows = (long long)B * Hh * Nb;
-  hipLaunchKernelGGL(bitmap_build, dim3((unsigned)((qrows + 3) / 4)), dim3(256), 0,
+  PRISM_LAUNCH("bitmap_build", bitmap_build, dim3((unsigned)((qrows + 3) / 4)), dim3(256), 0,
                      stream, counts, kv_idx, capacity, Nb, words, qrows, bits);
   if ((st = check_launch("bitmap_build")) != PRISM_OK) return st;
 
   dim3 grid(Nb, Hh, B);
   if (dtype == PRISM_BF16) {
-    hipLaunchKernelGGL(dkdv_bf16<D>, grid, dim3(256), 0, stream, (const uint16_t*)q,
+    PRISM_LAUNCH("dkdv_bf16", dkdv_bf16<D>, grid, dim3(256), 0, stream, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o,
                        lse, delta, perm, bits, words, Hh, N, scale, dk, dv);
     if ((st = check_launch("dkdv_bf16")) != PRISM_OK) return st;
-    hipLaunchKernelGGL(dq_bf16<D>, grid, dim3(256), 0, stream, (const uint16_t*)q,
+    PRISM_LAUNCH("dq_bf16", dq_bf16<D>, grid, dim3(256), 0, stream, (const uint16_t*)q,
                        (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o,
                        lse, delta, perm, counts, kv_idx, capacity, Hh, N, scale, dq);
     return check_launch("dq_bf16");
   }
-  hipLaunchKernelGGL(dkdv_f32<D>, grid, dim3(64), 0, stream, (const float*)q,
+  PRISM_LAUNCH("dkdv_f32", dkdv_f32<D>, grid, dim3(64), 0, stream, (const float*)q,
                      (const float*)k, (const float*)v, (const float*)d_o, lse, delta,
                      perm, bits, words, Hh, N, scale, dk, dv);
   if ((st = check_launch("dkdv_f32")) != PRISM_OK) return st;
-  hipLaunchKernelGGL(dq_f32<D>, grid, dim3(64), 0, stream, (const float*)q,
+  PRISM_LAUNCH("dq_f32", dq_f32<D>, grid, dim3(64), 0, stream, (const float*)q,
                      (const float*)k, (const float*)v, (const float*)d_o, lse, delta,
                      perm, counts, kv_idx, capacity, Hh, N, scale, dq);
   return check_launch("dq_f32");

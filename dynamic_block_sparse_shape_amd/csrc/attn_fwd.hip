@@ -257,20 +257,20 @@ prism_status launch_attn_fwd(const void* q, const void* k, const void* v,
   if (dtype == PRISM_BF16) {
     const float sl2 = scale * kLog2e;
     if (d == 128)
-      hipLaunchKernelGGL(attn_fwd_bf16<128>, grid, dim3(256), 0, stream,
+      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<128>, grid, dim3(256), 0, stream,
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                          perm, counts, kv_idx, capacity, Hh, N, sl2, (uint16_t*)o, lse);
     else
-      hipLaunchKernelGGL(attn_fwd_bf16<64>, grid, dim3(256), 0, stream,
+      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<64>, grid, dim3(256), 0, stream,
                          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                          perm, counts, kv_idx, capacity, Hh, N, sl2, (uint16_t*)o, lse);
   } else {
     if (d == 128)
-      hipLaunchKernelGGL(attn_fwd_f32<128>, grid, dim3(64), 0, stream,
+      PRISM_LAUNCH("attn_fwd_f32", attn_fwd_f32<128>, grid, dim3(64), 0, stream,
                          (const float*)q, (const float*)k, (const float*)v, perm,
                          counts, kv_idx, capacity, Hh, N, scale, (float*)o, lse);
     else
-      hipLaunchKernelGGL(attn_fwd_f32<64>, grid, dim3(64), 0, stream,
+      PRISM_LAUNCH("attn_fwd_f32", attn_fwd_f32<64>, grid, dim3(64), 0, stream,
                          (const float*)q, (const float*)k, (const float*)v, perm,
                          counts, kv_idx, capacity, Hh, N, scale, (float*)o, lse);
   }

@@ -194,7 +194,7 @@ prism_status launch_pool(const void* q, const void* k, const int32_t* perm,
                          int B, int Hh, int N, double* qm, double* km,
                          hipStream_t stream) {
   dim3 grid(N / 64, Hh, B);
-  hipLaunchKernelGGL((pool_blocks<E, D>), grid, dim3(kThreads), 0, stream,
+  PRISM_LAUNCH("pool_blocks", (pool_blocks<E, D>), grid, dim3(kThreads), 0, stream,
                      static_cast<const unsigned char*>(q),
                      static_cast<const unsigned char*>(k), perm, Hh, N, qm, km);
   return check_launch("pool_blocks");
@@ -217,20 +217,20 @@ prism_status launch_pool_proxy(const void* q, const void* k, int dtype,
 
   const int Nb = N / 64;
   dim3 g2(ceil_div(Nb, kTile), ceil_div(Nb, kTile), B * Hh);
-  hipLaunchKernelGGL(proxy_logits, g2, dim3(kThreads), 0, stream, q_mean,
+  PRISM_LAUNCH("proxy_logits", proxy_logits, g2, dim3(kThreads), 0, stream, q_mean,
                      k_mean, Nb, d, sqrt((double)d), proxy);
   st = check_launch("proxy_logits");
   if (st != PRISM_OK) return st;
 
   const unsigned rows = (unsigned)((long long)B * Hh * Nb);
   if (Nb <= 4 * kThreads)
-    hipLaunchKernelGGL(row_softmax<4>, dim3(rows), dim3(kThreads), 0, stream, proxy, Nb);
+    PRISM_LAUNCH("row_softmax", row_softmax<4>, dim3(rows), dim3(kThreads), 0, stream, proxy, Nb);
   else if (Nb <= 8 * kThreads)
-    hipLaunchKernelGGL(row_softmax<8>, dim3(rows), dim3(kThreads), 0, stream, proxy, Nb);
+    PRISM_LAUNCH("row_softmax", row_softmax<8>, dim3(rows), dim3(kThreads), 0, stream, proxy, Nb);
   else if (Nb <= 16 * kThreads)
-    hipLaunchKernelGGL(row_softmax<16>, dim3(rows), dim3(kThreads), 0, stream, proxy, Nb);
+    PRISM_LAUNCH("row_softmax", row_softmax<16>, dim3(rows), dim3(kThreads), 0, stream, proxy, Nb);
   else
-    hipLaunchKernelGGL(row_softmax<32>, dim3(rows), dim3(kThreads), 0, stream, proxy, Nb);
+    PRISM_LAUNCH("row_softmax", row_softmax<32>, dim3(rows), dim3(kThreads), 0, stream, proxy, Nb);
   return check_launch("row_softmax");
 }
 

@@ -14,6 +14,21 @@ void clear_error();
 // Wraps the launch status of the most recent kernel.
 prism_status check_launch(const char* what);
 
+// Optional per-kernel timing (prism_profile_* in include/prism.h): when
+// enabled, every launch is bracketed by two hipEvents on its stream.
+struct ProfScope {
+  int slot;
+  hipStream_t stream;
+  ProfScope(hipStream_t s, const char* name);
+  ~ProfScope();
+};
+
+#define PRISM_LAUNCH(NAME, KERNEL, GRID, BLOCK, SHM, STREAM, ...)          \
+  do {                                                                    \
+    prism::ProfScope prism_prof_scope_((STREAM), (NAME));                 \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHM, STREAM, __VA_ARGS__);    \
+  } while (0)
+
 #define PRISM_CHECK(cond, st, ...)            \
   do {                                        \
     if (!(cond)) return prism::fail(st, __VA_ARGS__); \

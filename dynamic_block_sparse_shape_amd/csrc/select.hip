@@ -387,16 +387,16 @@ prism_status launch_select(const double* proxy, int B, int Hh, int Nb,
                            int32_t* kv_idx, int capacity, hipStream_t stream) {
   const unsigned rows = (unsigned)((long long)B * Hh * Nb);
   if (Nb <= 4 * kThreads)
-    hipLaunchKernelGGL(select_rows<4>, dim3(rows), dim3(kThreads), 0, stream,
+    PRISM_LAUNCH("select_rows", select_rows<4>, dim3(rows), dim3(kThreads), 0, stream,
                        proxy, Nb, top_k, tau, counts, kv_idx, capacity);
   else if (Nb <= 8 * kThreads)
-    hipLaunchKernelGGL(select_rows<8>, dim3(rows), dim3(kThreads), 0, stream,
+    PRISM_LAUNCH("select_rows", select_rows<8>, dim3(rows), dim3(kThreads), 0, stream,
                        proxy, Nb, top_k, tau, counts, kv_idx, capacity);
   else if (Nb <= 16 * kThreads)
-    hipLaunchKernelGGL(select_rows<16>, dim3(rows), dim3(kThreads), 0, stream,
+    PRISM_LAUNCH("select_rows", select_rows<16>, dim3(rows), dim3(kThreads), 0, stream,
                        proxy, Nb, top_k, tau, counts, kv_idx, capacity);
   else
-    hipLaunchKernelGGL(select_rows<32>, dim3(rows), dim3(kThreads), 0, stream,
+    PRISM_LAUNCH("select_rows", select_rows<32>, dim3(rows), dim3(kThreads), 0, stream,
                        proxy, Nb, top_k, tau, counts, kv_idx, capacity);
   return check_launch("select_rows");
 }

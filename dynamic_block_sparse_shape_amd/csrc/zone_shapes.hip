@@ -340,10 +340,10 @@ prism_status launch_zone_shapes(const void* feat, const void* a2v, int dtype,
     rms = reinterpret_cast<double*>(static_cast<char*>(ws) + ((part + 255) / 256) * 256);
     dim3 grid(n_slices, g.nZ, B);
     if (dtype == PRISM_BF16)
-      hipLaunchKernelGGL(zone_feat_dev<uint16_t>, grid, dim3(kThreads), 0, stream,
+      PRISM_LAUNCH("zone_feat_dev", zone_feat_dev<uint16_t>, grid, dim3(kThreads), 0, stream,
                          static_cast<const unsigned char*>(feat), g, C, n_slices, partial);
     else
-      hipLaunchKernelGGL(zone_feat_dev<float>, grid, dim3(kThreads), 0, stream,
+      PRISM_LAUNCH("zone_feat_dev", zone_feat_dev<float>, grid, dim3(kThreads), 0, stream,
                          static_cast<const unsigned char*>(feat), g, C, n_slices, partial);
     prism_status st = check_launch("zone_feat_dev");
     if (st != PRISM_OK) return st;
@@ -351,10 +351,10 @@ prism_status launch_zone_shapes(const void* feat, const void* a2v, int dtype,
       const long long ntok = (long long)B * N;
       dim3 g2((unsigned)((ntok + 3) / 4));
       if (dtype == PRISM_BF16)
-        hipLaunchKernelGGL(token_rms<uint16_t>, g2, dim3(kThreads), 0, stream,
+        PRISM_LAUNCH("token_rms", token_rms<uint16_t>, g2, dim3(kThreads), 0, stream,
                            static_cast<const unsigned char*>(a2v), ntok, C, rms);
       else
-        hipLaunchKernelGGL(token_rms<float>, g2, dim3(kThreads), 0, stream,
+        PRISM_LAUNCH("token_rms", token_rms<float>, g2, dim3(kThreads), 0, stream,
                            static_cast<const unsigned char*>(a2v), ntok, C, rms);
       st = check_launch("token_rms");
       if (st != PRISM_OK) return st;
@@ -362,7 +362,7 @@ prism_status launch_zone_shapes(const void* feat, const void* a2v, int dtype,
       rms = nullptr;
     }
   }
-  hipLaunchKernelGGL(zone_finalize, dim3(g.nZ, B), dim3(kThreads), 0, stream, g, C,
+  PRISM_LAUNCH("zone_finalize", zone_finalize, dim3(g.nZ, B), dim3(kThreads), 0, stream, g, C,
                      n_slices, partial, rms, lam, fixed_shape, zone_shape, perm,
                      inv_perm, zone_stats);
   return check_launch("zone_finalize");

@@ -63,6 +63,19 @@ const char* prism_last_error(void);
 /* ABI version (major * 100 + minor). */
 int prism_version(void);
 
+/* Optional per-kernel timing, off by default.  While enabled, every kernel
+ * the library launches is bracketed by two hipEvents recorded on its
+ * stream (up to 4096 launches after the last enable / reset; later launches
+ * are not recorded).  Events are created on the device current at the first
+ * enable; use one device.  prism_profile_ms(i) waits for launch i to finish
+ * and returns its duration in ms (-1 on error).  Not for concurrent use from
+ * several host threads. */
+int prism_profile_enable(int on);
+void prism_profile_reset(void);
+int prism_profile_count(void);
+const char* prism_profile_name(int i);
+float prism_profile_ms(int i);
+
 /* The 13 candidate block shapes as (t, h, w) triples, written to
  * out_thw[3*id + {0,1,2}] (host memory, 39 ints).  Returns 13.  The pages
  * name (4,4,4), (8,2,4) and (2,4,8); the table holds every power-of-two

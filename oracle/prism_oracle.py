@@ -380,13 +380,15 @@ def sparse_attn_fwd(q, k, v, perm, lists, scale: Optional[float] = None,
     return o, lse
 
 
-def sparse_attn_bwd(q, k, v, do, perm, lists, scale: Optional[float] = None):
+def sparse_attn_bwd(q, k, v, do, perm, lists, scale: Optional[float] = None,
+                    query_blocks: Optional[Sequence[int]] = None):
     """Gradients of the block-sparse attention; the selection is constant.
 
     Reading R15: top-k / CDF routing is discrete, so no gradient flows into
     it.  D_r = <dO_r, o_r>; P = exp(s - LSE); dV = P^T dO; dP = dO V^T;
     dS = P * (dP - D); dQ = dS K * scale; dK = dS^T Q * scale.
-    Returns dq, dk, dv [N, d] (fp64).
+    Returns dq, dk, dv [N, d] (fp64).  With ``query_blocks`` only those query
+    blocks contribute (their dQ rows and their share of dK / dV).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -399,7 +401,8 @@ def sparse_attn_bwd(q, k, v, do, perm, lists, scale: Optional[float] = None):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for i in range(nb):
+    blocks = range(nb) if query_blocks is None else query_blocks
+    for i in blocks:
         rows = _block_rows(perm, i)
         cols = _kv_rows(perm, lists[i])
         s = (q[rows] @ k[cols].T) * scale

@@ -23,7 +23,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = P.lib()
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     # the Python binding carries the same names
