@@ -1,0 +1,271 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (all heads at once, same kernels, same buffers).
+
+The oracle computes what it can in seconds: the whole of stage 1 and the
+pooling; proxy scores and selection on sampled heads; attention rows of
+sampled query blocks; dK / dV of sampled KV blocks (those selected by few
+query blocks, so their exact gradient is cheap).  On top, properties that
+hold at any size are checked for every head: every proxy row sums to 1,
+every selection keeps the top-k floor and reaches the CDF mass, and the
+gradient sum rules sum_c dV_c = sum_r dO_r and sum_c dK_c = 0 (rows of P sum
+to one, and each row of dS sums to zero).
+"""
+import math
+import os
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import dynamic_block_sparse_shape_amd as P
+from oracle import prism_oracle as po
+from synth import CONFIGS, make_inputs
+from tests.gpu_util import assert_close, err_stats, widen
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}      # generated inputs (one workload at a time)
+_STAGE1 = {}     # oracle stage-1 results by seed (shared by fwd / training)
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _inputs(cid):
+    seed_key = (CONFIGS[cid]["seed"], CONFIGS[cid]["backward"])
+    if seed_key not in _CACHE:
+        _CACHE.clear()
+        t = time.time()
+        _CACHE[seed_key] = make_inputs(cid, with_grad=CONFIGS[cid]["backward"])
+        _print(f"  inputs of {CONFIGS[cid]['name']} in {time.time() - t:.1f} s")
+    return _CACHE[seed_key]
+
+
+def _oracle_stage1(x):
+    key = x.cfg["seed"]
+    if key in _STAGE1:
+        return _STAGE1[key]
+    cfg = x.cfg
+    T, H, W = cfg["T"], cfg["H"], cfg["W"]
+    if not cfg["dynamic"]:
+        out = po.zone_shapes(None, None, T, H, W, fixed_shape=cfg["fixed_shape"])
+    else:
+        zones = po.zone_tiling(T, H, W)
+        F = x.feat[0].reshape(T, H, W, -1)
+        A = x.a2v[0].reshape(T, H, W, -1)
+
+        def one(z):
+            (t0, h0, w0), e = zones[z]
+            sl = (slice(t0, t0 + e[0]), slice(h0, h0 + e[1]), slice(w0, w0 + e[2]))
+            st = po.zone_statistics(widen(F[sl]), widen(A[sl]))
+            sid, margin = po.choose_shape(st, e)
+            return st, sid, margin
+
+        t = time.time()
+        with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as pool:
+            res = list(pool.map(one, range(len(zones))))
+        ids = np.array([r[1] for r in res])
+        out = dict(zone_shape=ids, stats=np.stack([r[0] for r in res]),
+                   margin=np.array([r[2] for r in res]), zones=zones,
+                   perm=po.block_permutation(T, H, W, zones, ids))
+        _print(f"  oracle stage 1 in {time.time() - t:.1f} s")
+    _STAGE1[key] = out
+    return out
+
+
+def _dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def _run_gpu(x, backward):
+    """The whole path, all heads, as the benchmark launches it."""
+    cfg = x.cfg
+    T, H, W = cfg["T"], cfg["H"], cfg["W"]
+    q, k, v = _dev(x.q), _dev(x.k), _dev(x.v)
+    if cfg["dynamic"]:
+        zs, perm, _, stats = P.zone_shapes(_dev(x.feat), _dev(x.a2v), T, H, W)
+    else:
+        zs, perm, _, stats = P.zone_shapes(None, None, T, H, W,
+                                           fixed_shape=cfg["fixed_shape"])
+    qm, km, proxy = P.pool_blocks(q, k, perm)
+    counts, kv = P.select_blocks(proxy, cfg["top_k"], cfg["cdf_threshold"])
+    o, lse = P.sparse_attn_fwd(q, k, v, perm, counts, kv)
+    grads = None
+    if backward:
+        grads = P.sparse_attn_bwd(q, k, v, o, _dev(x.do), lse, perm, counts, kv)
+    torch.cuda.synchronize()
+    return dict(zs=zs, perm=perm, stats=stats, qm=qm, km=km, proxy=proxy,
+                counts=counts, kv=kv, o=o, lse=lse, grads=grads)
+
+
+def _check_stage1(x, g, ref):
+    assert np.array_equal(g["perm"][0].cpu().numpy(), ref["perm"])
+    if x.cfg["dynamic"]:
+        assert ref["margin"].min() > po.REL_MARGIN_FLAG, ref["margin"].min()
+        assert np.array_equal(g["zs"][0].cpu().numpy(), ref["zone_shape"])
+        np.testing.assert_allclose(g["stats"][0].cpu().numpy(), ref["stats"],
+                                   rtol=1e-10, atol=1e-14)
+        hist = np.bincount(ref["zone_shape"], minlength=13)
+        _print("  shape histogram", hist.tolist())
+        assert (hist > 0).sum() >= 5
+
+
+def _check_routing(x, g, perm, heads):
+    cfg = x.cfg
+    qm, km = g["qm"].cpu().numpy(), g["km"].cpu().numpy()
+    counts = g["counts"].cpu().numpy()
+    routes = {}
+    for h in range(cfg["Hh"]):
+        rq = po.pool_blocks(widen(x.q[0, h]), perm)
+        rk = po.pool_blocks(widen(x.k[0, h]), perm)
+        assert np.array_equal(qm[0, h], rq) and np.array_equal(km[0, h], rk), h
+    # every head: selection invariants on the GPU's own proxy
+    nb = counts.shape[-1]
+    assert counts.min() >= max(1, min(cfg["top_k"], nb)) and counts.max() <= nb
+    for h in heads:
+        rq, rk = widen(x.q[0, h]), widen(x.k[0, h])
+        route = po.route_head(rq, rk, perm, cfg["top_k"], cfg["cdf_threshold"])
+        gp = g["proxy"][0, h].cpu().numpy()
+        rp = route["proxy"]
+        np.testing.assert_allclose(gp, rp, rtol=1e-11, atol=1e-300)
+        # largest relative difference of the two fp64 proxies: a decision
+        # whose relative margin exceeds it by 100x cannot flip
+        pos = rp > 1e-250
+        eps = float(np.max(np.abs(gp[pos] - rp[pos]) / rp[pos]))
+        kvh = g["kv"][0, h].cpu().numpy()
+        d = route["diag"]
+        thr = 100.0 * eps + 1e-14
+        ok = (d["set_gap"] > thr) & (d["cdf_gap"] > thr)
+        _print(f"  head {h}: rows {nb}, proxy rel diff {eps:.1e}, min set gap "
+               f"{d['set_gap'].min():.1e}, min cdf gap {d['cdf_gap'].min():.1e}, "
+               f"undecidable rows {int((~ok).sum())}, mean count "
+               f"{route['counts'].mean():.1f}")
+        assert (~ok).sum() <= 2
+        bad_rows, bad_kv = set(), set()
+        for i in range(nb):
+            c = counts[0, h, i]
+            if ok[i]:
+                assert c == route["counts"][i], (h, i)
+                assert np.array_equal(kvh[i, :c], route["lists"][i]), (h, i)
+            else:
+                # undecidable at fp64 resolution: the GPU's choice must still
+                # be a valid selection on the oracle's scores
+                sel = kvh[i, :c]
+                assert np.all(np.diff(sel) > 0) and c >= min(cfg["top_k"], nb)
+                assert abs(int(c) - int(route["counts"][i])) <= 1
+                rest = np.setdiff1d(np.arange(nb), sel)
+                if rest.size:
+                    assert rp[i, sel].min() >= rp[i, rest].max() * (1 - thr)
+                if not np.array_equal(sel, route["lists"][i]):
+                    bad_rows.add(i)
+                    bad_kv.update(sel.tolist())
+                    bad_kv.update(route["lists"][i].tolist())
+        route["bad_rows"], route["bad_kv"] = bad_rows, bad_kv
+        routes[h] = route
+    return routes
+
+
+def _check_forward(x, g, perm, routes, nsample, bf16):
+    rng = np.random.default_rng(0)
+    worst = (0.0, 0.0)
+    for h, route in routes.items():
+        nb = len(route["counts"])
+        good = np.array([i for i in range(nb) if i not in route["bad_rows"]])
+        blocks = sorted(rng.choice(good, size=min(nsample, good.size),
+                                   replace=False).tolist())
+        ro, rl = po.sparse_attn_fwd(widen(x.q[0, h]), widen(x.k[0, h]),
+                                    widen(x.v[0, h]), perm, route["lists"],
+                                    query_blocks=blocks)
+        rows = np.concatenate([perm[64 * i:64 * (i + 1)] for i in blocks])
+        go = g["o"][0, h].float().cpu().numpy()[rows]
+        gl = g["lse"][0, h].cpu().numpy()[rows]
+        r1 = assert_close(go, ro[rows], bf16, f"o head {h}")
+        r2 = assert_close(gl, rl[rows], bf16, f"lse head {h}")
+        worst = (max(worst[0], r1[0]), max(worst[1], r1[1]))
+    _print(f"  forward sampled: worst rel L2 {worst[0]:.2e}, max-abs {worst[1]:.2e}")
+
+
+def _check_backward(x, g, perm, routes, nsample):
+    cfg = x.cfg
+    dq, dk, dv = (t.cpu().numpy() for t in g["grads"])
+    # sum rules on every head
+    for h in range(cfg["Hh"]):
+        sdo = widen(x.do[0, h]).sum(0)
+        rel, mx = err_stats(dv[0, h].astype(np.float64).sum(0), sdo)
+        assert rel < 1e-3, ("sum dV", h, rel)
+        sk = np.abs(dk[0, h].astype(np.float64).sum(0)).max()
+        scale_k = np.abs(dk[0, h]).sum(0).max()
+        assert sk < 1e-3 * scale_k, ("sum dK", h, sk, scale_k)
+    rng = np.random.default_rng(1)
+    for h, route in routes.items():
+        nb = len(route["counts"])
+        q0, k0, v0, do0 = (widen(a[0, h]) for a in (x.q, x.k, x.v, x.do))
+        # dQ of sampled query blocks: exact with only their own lists
+        good = np.array([i for i in range(nb) if i not in route["bad_rows"]])
+        blocks = sorted(rng.choice(good, size=min(nsample, good.size),
+                                   replace=False).tolist())
+        rq, _, _ = po.sparse_attn_bwd(q0, k0, v0, do0, perm, route["lists"],
+                                      query_blocks=blocks)
+        rows = np.concatenate([perm[64 * i:64 * (i + 1)] for i in blocks])
+        assert_close(dq[0, h][rows], rq[rows], True, f"dq head {h}")
+        # dK / dV of the least-used KV blocks: every query block using them
+        users = [[] for _ in range(nb)]
+        for i, L in enumerate(route["lists"]):
+            for j in L:
+                users[j].append(i)
+        used = [j for j in range(nb) if users[j] and j not in route["bad_kv"]]
+        used.sort(key=lambda j: len(users[j]))
+        picks = used[:3]
+        qb = sorted(set(i for j in picks for i in users[j]))
+        _, rk, rv = po.sparse_attn_bwd(q0, k0, v0, do0, perm, route["lists"],
+                                       query_blocks=qb)
+        cols = np.concatenate([perm[64 * j:64 * (j + 1)] for j in picks])
+        assert_close(dk[0, h][cols], rk[cols], True, f"dk head {h}")
+        assert_close(dv[0, h][cols], rv[cols], True, f"dv head {h}")
+        _print(f"  backward head {h}: dq {len(blocks)} blocks, dk/dv KV blocks "
+               f"{picks} used by {[len(users[j]) for j in picks]} query blocks")
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3])
+def test_forward_full_size(cid):
+    x = _inputs(cid)
+    _print(f"full-size forward {x.cfg['name']}")
+    t = time.time()
+    g = _run_gpu(x, backward=False)
+    _print(f"  gpu path in {time.time() - t:.1f} s")
+    ref = _oracle_stage1(x)
+    _check_stage1(x, g, ref)
+    perm = ref["perm"]
+    heads = [0, x.cfg["Hh"] - 1]
+    routes = _check_routing(x, g, perm, heads)
+    _check_forward(x, g, perm, routes, nsample=12, bf16=True)
+
+
+@pytest.mark.parametrize("cid", [4, 5])
+def test_training_full_size(cid):
+    x = _inputs(cid)
+    _print(f"full-size training {x.cfg['name']}")
+    t = time.time()
+    g = _run_gpu(x, backward=True)
+    _print(f"  gpu path in {time.time() - t:.1f} s")
+    ref = _oracle_stage1(x)
+    _check_stage1(x, g, ref)
+    perm = ref["perm"]
+    routes = _check_routing(x, g, perm, [1])
+    _check_forward(x, g, perm, routes, nsample=6, bf16=True)
+    _check_backward(x, g, perm, routes, nsample=6)
+
+
+def test_tiny_fp32_full():
+    """The tiny fp32 workload: everything checked, every row."""
+    x = _inputs(0)
+    g = _run_gpu(x, backward=False)
+    ref = _oracle_stage1(x)
+    _check_stage1(x, g, ref)
+    routes = _check_routing(x, g, ref["perm"], [0, 1])
+    _check_forward(x, g, ref["perm"], routes, nsample=4, bf16=False)
