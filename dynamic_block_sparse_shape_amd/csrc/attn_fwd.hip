@@ -6,197 +6,193 @@
 // one online-softmax pass; README "Overview": each query block has its own
 // budget of blocks.
 //
-// bf16 path (gfx950 MFMA, v_mfma_f32_16x16x32_bf16, fp32 accumulation):
-//   one workgroup (4 waves) per (b, h, query block); wave w owns query rows
-//   16w..16w+15, held in registers as the B operand.  For each listed KV
-//   block the workgroup gathers K (row-major) and V (transposed) through
-//   perm into LDS.  Each wave computes S^T = K Q^T (kv x q), so every lane
-//   holds 16 scores of one query and the row statistics need only two
-//   cross-lane steps; the KV rows feeding the M-tiles are ordered so that
-//   the lane's scores are already the B operand of O^T += V^T P^T.
+// bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//   every wave computes S^T = K Q^T (kv x q), so a lane holds 16 scores of
+//   one query and the row statistics need one cross-lane step; the K rows
+//   feeding the M-rows are ordered (tiles::slot_of) so that the lane's
+//   probabilities are already the B operand of O^T += V^T P^T -- P never
+//   goes through LDS.
 // fp32 path: one thread per query row, plain fp32 arithmetic (reference
 //   precision for small problems).
-#include "prism_internal.h"
+#include "attn_tiles.h"
 
 namespace prism {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// KV row feeding M-row m of M-tile mt, chosen so that the C layout of the
-// score tiles (lane group g holds M-rows 4g..4g+3) lands each lane's scores
-// on kv slots 32*(mt/2) + 8g + 4*(mt%2) + r -- eight consecutive kv per
-// lane group per 32-wide k-step of the P*V product.
-__device__ __forceinline__ int kv_of(int mt, int m) {
-  return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
-}
-
+// One workgroup (4 waves) per (b, h, query block).  Wave w = (qh, kh):
+// queries 32*qh .. 32*qh+31 against KV rows 32*kh .. 32*kh+31 of every
+// listed block, so every 32x32 MFMA tile is reused over a 128-deep (S) or
+// 32-deep (P*V) contraction and each K/V byte in LDS is read by two waves.
+// The two kh waves of a query half keep separate online-softmax states and
+// are merged once at the end (exactly as a split over KV).  K and V stay
+// row-major in LDS; V^T fragments come from ds_read_b64_tr_b16.  Blocks are
+// staged two ahead through registers.
 template <int D>
-struct FwdSmem {
-  static constexpr int KLD = D + 8;   // K row stride (bf16 elements)
-  static constexpr int VLD = 64 + 8;  // V^T row stride
-  uint16_t K[64 * KLD];
-  uint16_t Vt[D * VLD];
-  int rows[64];
-};
-
-template <int D>
-__global__ __launch_bounds__(256) void attn_fwd_bf16(
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ kv_idx,
-    int capacity, int Hh, int N, float scale_log2, uint16_t* __restrict__ o,
-    float* __restrict__ lse) {
-  constexpr int KS = D / 32;   // k-steps of Q K^T
-  constexpr int DT = D / 16;   // d tiles of O^T
-  constexpr int KLD = FwdSmem<D>::KLD;
-  constexpr int VLD = FwdSmem<D>::VLD;
-  __shared__ __align__(16) FwdSmem<D> sm;
+    int capacity, int Hh, int N, long long total /* B * Hh */, float scale_log2,
+    uint16_t* __restrict__ o, float* __restrict__ lse) {
+  using namespace tiles;
+  using TL = Tile<D>;
+  constexpr int KS = D / 16;     // k-steps of S^T = K Q^T
+  constexpr int DT = D / 32;     // 32-row d tiles of O^T
+  __shared__ __align__(16) unsigned char smem[2 * TL::kBytes];
+  __shared__ float sm_m[2][32], sm_l[2][32];
+  unsigned char* sk = smem;
+  unsigned char* sv = smem + TL::kBytes;
 
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int Nb = N / 64;
+  long long bh;
+  int i;
+  if (!xcd_item(Nb, total, bh, i)) return;
+  const int b = (int)(bh / Hh);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c16 = lane & 15;
-  const long long head = ((long long)b * Hh + h) * N;   // row offset
+  const int qh = wave & 1, kh = wave >> 1;
+  const int c = lane & 31, hf = lane >> 5, j16 = lane & 15, grp = lane >> 4;
+  const long long head = bh * N;
   const int32_t* pb = perm + (long long)b * N;
 
-  const int qrow = pb[64 * i + 16 * wave + c16];
+  const int qrow = pb[64 * i + 32 * qh + c];
   bf16x8 qreg[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
-    qreg[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(
-        q + (head + qrow) * D + 32 * ks + 8 * g));
+    qreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+        q + (head + qrow) * D + 16 * ks + 8 * hf));
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 oacc[DT];
-#pragma unroll
-  for (int t = 0; t < DT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const long long rowid = ((long long)b * Hh + h) * Nb + i;
+  const long long rowid = bh * Nb + i;
   const int cnt = counts[rowid];
   const int32_t* lst = kv_idx + rowid * (long long)capacity;
 
-  for (int t = 0; t < cnt; ++t) {
-    const int j = lst[t];
-    __syncthreads();
-    if (tid < 64) sm.rows[tid] = pb[64 * j + tid];
-    __syncthreads();
-    // K: 64 rows x D bf16, 16-byte pieces
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[DT];
 #pragma unroll
-    for (int c = tid; c < 64 * (D / 8); c += 256) {
-      const int r = c / (D / 8), piece = c % (D / 8);
-      *reinterpret_cast<uint4*>(&sm.K[r * KLD + piece * 8]) =
-          *reinterpret_cast<const uint4*>(k + (head + sm.rows[r]) * D + piece * 8);
-    }
-    // V^T: a thread takes 8 d-values of 4 consecutive kv rows
-    for (int c = tid; c < (D / 8) * 16; c += 256) {
-      const int dc = c % (D / 8), rg = c / (D / 8);
-      uint4 r4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        r4[e] = *reinterpret_cast<const uint4*>(v + (head + sm.rows[4 * rg + e]) * D + dc * 8);
-      const uint16_t* s0 = reinterpret_cast<const uint16_t*>(&r4[0]);
-      const uint16_t* s1 = reinterpret_cast<const uint16_t*>(&r4[1]);
-      const uint16_t* s2 = reinterpret_cast<const uint16_t*>(&r4[2]);
-      const uint16_t* s3 = reinterpret_cast<const uint16_t*>(&r4[3]);
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        uint2 pk;
-        pk.x = (uint32_t)s0[e8] | ((uint32_t)s1[e8] << 16);
-        pk.y = (uint32_t)s2[e8] | ((uint32_t)s3[e8] << 16);
-        *reinterpret_cast<uint2*>(&sm.Vt[(dc * 8 + e8) * VLD + 4 * rg]) = pk;
-      }
-    }
-    __syncthreads();
+  for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
+  const int krow = 32 * kh + slot_of(c);   // K row feeding this lane's M-row
 
-    // S^T = K Q^T
-    f32x4 s[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* krow = &sm.K[kv_of(mt, c16) * KLD + 8 * g];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(krow + 32 * ks)), qreg[ks],
-            s[mt], 0, 0, 0);
+  Stage<D> kA, vA, kB, vB;
+  int rows_n[TL::kPerThread];
+  int j_n = 0;
+  // prologue: blocks 0 and 1 in flight, rows of block 2, id of block 3
+  {
+    int r0[TL::kPerThread];
+    stage_rows<D>(r0, pb, lst[0], tid);
+    stage_load<D>(kA, k, head, r0, tid);
+    stage_load<D>(vA, v, head, r0, tid);
+    if (cnt > 1) {
+      stage_rows<D>(r0, pb, lst[1], tid);
+      stage_load<D>(kB, k, head, r0, tid);
+      stage_load<D>(vB, v, head, r0, tid);
     }
-    // online softmax (log2 domain) for query c16
+    if (cnt > 2) stage_rows<D>(rows_n, pb, lst[2], tid);
+    if (cnt > 3) j_n = lst[3];
+  }
+
+// One KV block: publish the staged block t to LDS, refill the stage with
+// block t+2, advance the row / id prefetch, then compute on LDS.
+#define PRISM_FWD_STEP(T_, KS_, VS_)                                        \
+  {                                                                         \
+    const int tt = (T_);                                                    \
+    __syncthreads();                                                        \
+    stage_store<D>(KS_, sk, tid);                                           \
+    stage_store<D>(VS_, sv, tid);                                           \
+    __syncthreads();                                                        \
+    if (tt + 2 < cnt) {                                                     \
+      stage_load<D>(KS_, k, head, rows_n, tid);                             \
+      stage_load<D>(VS_, v, head, rows_n, tid);                             \
+    }                                                                       \
+    if (tt + 3 < cnt) stage_rows<D>(rows_n, pb, j_n, tid);                  \
+    if (tt + 4 < cnt) j_n = lst[tt + 4];                                    \
+    compute_block();                                                        \
+  }
+
+  auto compute_block = [&]() __attribute__((always_inline)) {
+    // S^T (32 kv x 32 q) = K_half Q_half^T
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      s = mfma32(lds_row8<D>(sk, krow, 2 * ks + hf), qreg[ks], s);
     float mx = -INFINITY;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[mt][r] *= scale_log2;
-        mx = fmaxf(mx, s[mt][r]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    for (int r = 0; r < 16; ++r) {
+      s[r] *= scale_log2;
+      mx = fmaxf(mx, s[r]);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
     const float alpha = exp2f(m_run - m_new);
     float rs = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        s[mt][r] = exp2f(s[mt][r] - m_new);
-        rs += s[mt][r];
-      }
-    rs += __shfl_xor(rs, 16, 64);
+    for (int r = 0; r < 16; ++r) {
+      s[r] = exp2f(s[r] - m_new);
+      rs += s[r];
+    }
     rs += __shfl_xor(rs, 32, 64);
     l_run = l_run * alpha + rs;
     m_run = m_new;
 #pragma unroll
     for (int t2 = 0; t2 < DT; ++t2) oacc[t2] *= alpha;
-
-    // P^T as the B operand: k-step ks2 covers kv 32*ks2 .. 32*ks2+31
-    bf16x8 pbf[2];
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      uint4 u;
-      uint32_t* uw = reinterpret_cast<uint32_t*>(&u);
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        uw[r / 2] = (uint32_t)f32_to_bf16(s[2 * ks2][r]) |
-                    ((uint32_t)f32_to_bf16(s[2 * ks2][r + 1]) << 16);
-        uw[2 + r / 2] = (uint32_t)f32_to_bf16(s[2 * ks2 + 1][r]) |
-                        ((uint32_t)f32_to_bf16(s[2 * ks2 + 1][r + 1]) << 16);
-      }
-      pbf[ks2] = as_bf16x8(u);
-    }
-    // O^T += V^T P^T
+    const bf16x8 p0 = pack8(s, 0), p1 = pack8(s, 1);
+    // O^T (d x 32 q) += V_half^T P^T
 #pragma unroll
     for (int mt = 0; mt < DT; ++mt) {
-      const uint16_t* vrow = &sm.Vt[(16 * mt + c16) * VLD + 8 * g];
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-        oacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(vrow + 32 * ks2)), pbf[ks2],
-            oacc[mt], 0, 0, 0);
+      const int d0 = 32 * mt + 16 * (grp & 1);
+      const int r0 = 32 * kh + 8 * (grp >> 1);
+      oacc[mt] = mfma32(lds_tr8<D>(sv, r0, d0, j16), p0, oacc[mt]);
+      oacc[mt] = mfma32(lds_tr8<D>(sv, r0 + 16, d0, j16), p1, oacc[mt]);
     }
-  }
+  };
 
-  // O[q][16mt + 4g + r] = oacc[mt][r] / l
-  const float inv_l = 1.f / l_run;
-  uint16_t* orow = o + (head + qrow) * D;
-#pragma unroll
-  for (int mt = 0; mt < DT; ++mt) {
-    uint2 pk;
-    pk.x = (uint32_t)f32_to_bf16(oacc[mt][0] * inv_l) |
-           ((uint32_t)f32_to_bf16(oacc[mt][1] * inv_l) << 16);
-    pk.y = (uint32_t)f32_to_bf16(oacc[mt][2] * inv_l) |
-           ((uint32_t)f32_to_bf16(oacc[mt][3] * inv_l) << 16);
-    *reinterpret_cast<uint2*>(orow + 16 * mt + 4 * g) = pk;
+  int t = 0;
+  for (; t + 1 < cnt; t += 2) {
+    PRISM_FWD_STEP(t, kA, vA)
+    PRISM_FWD_STEP(t + 1, kB, vB)
   }
-  if (g == 0) lse[head + qrow] = (m_run + log2f(l_run)) * kLn2;
+  if (t < cnt) PRISM_FWD_STEP(t, kA, vA)
+#undef PRISM_FWD_STEP
+
+  // merge the two KV halves: waves kh = 1 hand over (m, l, O) through LDS
+  __syncthreads();
+  // 2 waves x 64 lanes x (D/2) floats = 2 * TL::kBytes
+  float* xo = reinterpret_cast<float*>(smem);
+  if (kh == 1) {
+    if (hf == 0) {
+      sm_m[qh][c] = m_run;
+      sm_l[qh][c] = l_run;
+    }
+#pragma unroll
+    for (int mt = 0; mt < DT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        xo[((qh * 64 + lane) * DT + mt) * 16 + r] = oacc[mt][r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m2 = sm_m[qh][c], l2 = sm_l[qh][c];
+    const float m = fmaxf(m_run, m2);
+    const float a1 = exp2f(m_run - m), a2 = exp2f(m2 - m);
+    const float l = l_run * a1 + l2 * a2;
+    const float inv_l = 1.f / l;
+    uint16_t* orow = o + (head + qrow) * D;
+#pragma unroll
+    for (int mt = 0; mt < DT; ++mt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float vals[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int r = 4 * a + bb;
+          vals[bb] = (oacc[mt][r] * a1 +
+                      xo[((qh * 64 + lane) * DT + mt) * 16 + r] * a2) * inv_l;
+        }
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(vals[0]) | ((uint32_t)f32_to_bf16(vals[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(vals[2]) | ((uint32_t)f32_to_bf16(vals[3]) << 16);
+        *reinterpret_cast<uint2*>(orow + 32 * mt + 8 * a + 4 * hf) = pk;
+      }
+    if (hf == 0) lse[head + qrow] = (m + log2f(l)) * kLn2;
+  }
 }
 
 // fp32 reference-precision path: one thread per query row.
@@ -255,15 +251,19 @@ prism_status launch_attn_fwd(const void* q, const void* k, const void* v,
                              hipStream_t stream) {
   dim3 grid(N / 64, Hh, B);
   if (dtype == PRISM_BF16) {
-    const float sl2 = scale * kLog2e;
+    const float sl2 = scale * tiles::kLog2e;
+    const long long total = (long long)B * Hh;   // (batch, head) pairs
+    const dim3 g1(tiles::xcd_grid(N / 64, total));
     if (d == 128)
-      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<128>, grid, dim3(256), 0, stream,
-                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                         perm, counts, kv_idx, capacity, Hh, N, sl2, (uint16_t*)o, lse);
+      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<128>, g1, dim3(256), 0, stream,
+                   (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                   perm, counts, kv_idx, capacity, Hh, N, total, sl2,
+                   (uint16_t*)o, lse);
     else
-      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<64>, grid, dim3(256), 0, stream,
-                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                         perm, counts, kv_idx, capacity, Hh, N, sl2, (uint16_t*)o, lse);
+      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<64>, g1, dim3(256), 0, stream,
+                   (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                   perm, counts, kv_idx, capacity, Hh, N, total, sl2,
+                   (uint16_t*)o, lse);
   } else {
     if (d == 128)
       PRISM_LAUNCH("attn_fwd_f32", attn_fwd_f32<128>, grid, dim3(64), 0, stream,

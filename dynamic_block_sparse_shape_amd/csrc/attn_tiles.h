@@ -1,0 +1,171 @@
+// Building blocks of the gfx950 block-sparse attention kernels.
+//
+// * 64-row bf16 tiles (one 64-token block of K, V, Q or dO) live row-major in
+//   LDS with an XOR swizzle of their 16-byte pieces, so that both access
+//   patterns below are free of bank conflicts:
+//     - row-operand reads: ds_read_b128 of one 16-byte piece from 16
+//       different rows per quarter-wave;
+//     - transposed-operand reads: ds_read_b64_tr_b16 (gfx950), where each
+//       quarter-wave reads 8 bytes from 4 consecutive rows x 4 columns and
+//       the hardware hands every lane 4 consecutive rows of one column.
+// * A workgroup of 256 threads stages a tile with 16-byte global loads held
+//   in registers (two blocks ahead), then one ds_write_b128 per piece.
+// * MFMA v_mfma_f32_32x32x16_bf16 operand layouts (lane l, c = l % 32,
+//   h = l / 32): A[i][k] holds i = c, k = 8h .. 8h+7; B[k][j] holds j = c,
+//   k = 8h .. 8h+7; C[i][j] holds j = c and rows i = 8a + 4h + b in register
+//   4a + b (a, b in 0..3).
+#pragma once
+
+#include "prism_internal.h"
+
+namespace prism {
+namespace tiles {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of the 32-row operand that feeds M-row i of a 32x32 tile.  With this
+// order the C-layout registers 8s..8s+7 of a lane hold rows 16s + 8h + e
+// (e = 0..7), i.e. exactly the B operand (k = 8h + e) of the next product
+// over the same 32 rows, k-step s.
+__device__ __forceinline__ int slot_of(int i) {
+  const int a = i >> 3, hh = (i >> 2) & 1, b = i & 3;
+  return 16 * (a >> 1) + 8 * hh + 4 * (a & 1) + b;
+}
+
+template <int D>
+struct Tile {
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kPieces = kRowBytes / 16;          // 16-byte pieces per row
+  static constexpr int kBytes = 64 * kRowBytes;
+  static constexpr int kPerThread = 64 * kPieces / 256;   // pieces per thread
+
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (kPieces == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+    else return (r >> 1) & (kPieces - 1);
+  }
+  // byte offset of (row r, 16-byte piece p)
+  __device__ static __forceinline__ int off(int r, int p) {
+    return r * kRowBytes + ((p ^ swz(r)) << 4);
+  }
+  // byte offset of the 8 bytes holding columns d .. d+3 of row r (d % 4 == 0)
+  __device__ static __forceinline__ int off8(int r, int d) {
+    return off(r, d >> 3) + ((d & 4) << 1);
+  }
+  // row of piece slot t of this thread
+  __device__ static __forceinline__ int row_of(int tid, int t) {
+    return (tid + 256 * t) / kPieces;
+  }
+  __device__ static __forceinline__ int piece_of(int tid) {
+    return tid % kPieces;
+  }
+};
+
+// 16-byte piece of a row-operand fragment: ds_read_b128
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row8(const unsigned char* tile, int r,
+                                          int p) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(tile + Tile<D>::off(r, p)));
+}
+
+// Transposed fragment for an A or B operand over 8 consecutive tile rows:
+// lane (quarter-wave lane j = l % 16) receives rows r0 .. r0+7 of column
+// d0 + j.  Two ds_read_b64_tr_b16, each covering 4 rows.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr8(const unsigned char* tile, int r0,
+                                         int d0, int j) {
+  const int r = r0 + (j >> 2);
+  const int d = d0 + 4 * (j & 3);
+  // generic -> LDS address space (the tile is a __shared__ array)
+  lds_bf16x4* p0 = (lds_bf16x4*)(tile + Tile<D>::off8(r, d));
+  lds_bf16x4* p1 = (lds_bf16x4*)(tile + Tile<D>::off8(r + 4, d));
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Global -> register staging of one 64-row tile (rows gathered through
+// row indices held by the thread).
+template <int D>
+struct Stage {
+  u32x4 v[Tile<D>::kPerThread];   // clang vectors: promotable to registers
+};
+
+template <int D>
+__device__ __forceinline__ void stage_load(Stage<D>& s,
+                                           const uint16_t* __restrict__ src,
+                                           long long head, const int* rows,
+                                           int tid) {
+  const int p = Tile<D>::piece_of(tid);
+#pragma unroll
+  for (int t = 0; t < Tile<D>::kPerThread; ++t)
+    s.v[t] = *reinterpret_cast<const u32x4*>(
+        src + (head + rows[t]) * D + p * 8);
+}
+
+template <int D>
+__device__ __forceinline__ void stage_store(const Stage<D>& s,
+                                            unsigned char* tile, int tid) {
+  const int p = Tile<D>::piece_of(tid);
+#pragma unroll
+  for (int t = 0; t < Tile<D>::kPerThread; ++t)
+    *reinterpret_cast<u32x4*>(tile + Tile<D>::off(Tile<D>::row_of(tid, t), p)) =
+        s.v[t];
+}
+
+// Row indices this thread needs to stage block j (perm[64 j + row]).
+template <int D>
+__device__ __forceinline__ void stage_rows(int* rows,
+                                           const int32_t* __restrict__ pb,
+                                           int j, int tid) {
+#pragma unroll
+  for (int t = 0; t < Tile<D>::kPerThread; ++t)
+    rows[t] = pb[64 * j + Tile<D>::row_of(tid, t)];
+}
+
+// Pack C-layout registers 8s .. 8s+7 into a bf16 B operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& c, int s) {
+  u32x4 u;
+  u.x = (uint32_t)f32_to_bf16(c[8 * s + 0]) | ((uint32_t)f32_to_bf16(c[8 * s + 1]) << 16);
+  u.y = (uint32_t)f32_to_bf16(c[8 * s + 2]) | ((uint32_t)f32_to_bf16(c[8 * s + 3]) << 16);
+  u.z = (uint32_t)f32_to_bf16(c[8 * s + 4]) | ((uint32_t)f32_to_bf16(c[8 * s + 5]) << 16);
+  u.w = (uint32_t)f32_to_bf16(c[8 * s + 6]) | ((uint32_t)f32_to_bf16(c[8 * s + 7]) << 16);
+  return as_bf16x8(u);
+}
+
+// Work item of this workgroup.  Workgroups are dealt round-robin to the 8
+// XCDs, so workgroup L runs on XCD L % 8.  Every head's Nb blocks are split
+// into 8 contiguous ranges, one per XCD, and heads are visited in order:
+// all XCDs work on the same head at the same time (its K / V, ~150 MB at
+// the 2K grid, stays in the MALL) and each XCD's L2 sees neighbouring
+// blocks, whose block lists overlap.  Returns false for padding items.
+__device__ __forceinline__ bool xcd_item(int Nb, long long heads, long long& bh,
+                                         int& i) {
+  const long long L = blockIdx.x;
+  const int c8 = (Nb + 7) / 8;
+  const long long s = L >> 3;
+  bh = s / c8;
+  i = (int)(L & 7) * c8 + (int)(s % c8);
+  return bh < heads && i < Nb;
+}
+inline unsigned xcd_grid(int Nb, long long heads) {
+  return (unsigned)(8LL * ((Nb + 7) / 8) * heads);
+}
+
+}  // namespace tiles
+}  // namespace prism
