@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of host time for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a 1 GiB device copy (reference dispatch "
+                         "for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -269,6 +272,15 @@ def main():
                                 B, Hh, N, d, -1.0, ptr(dq), ptr(dk), ptr(dv),
                                 ptr(wsb), wsb.numel(), sh)
         mark(5)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        _log("copy calibration: 3 x 1 GiB device copies done")
 
     for i in range(args.warmup):
         step()

@@ -11,81 +11,19 @@
 //   bitmap_clear /  column bitmaps: bit i of KV block j's word set when query
 //   bitmap_build    block i selected j -- the KV->query lists, read in
 //                   ascending i by the dK/dV kernel.
-//   dkdv_bf16       one workgroup per KV block; wave w owns 16 KV rows whose
-//                   K and V stay in registers; loops over the query blocks
-//                   that selected it (Q, Q^T, dO, dO^T staged in LDS).
-//   dq_bf16         one workgroup per query block; loops over its list
-//                   (K, K^T, V staged in LDS).
-// All products are v_mfma_f32_16x16x32_bf16 with fp32 accumulation; the
-// fp32 dtype uses plain per-thread kernels with the same structure.
+//   dkdv_bf16       one workgroup per KV block; loops over the query blocks
+//                   that selected it.
+//   dq_bf16         one workgroup per query block; loops over its list.
+// Both use v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulation, row-major
+// swizzled LDS tiles with transposed fragments from ds_read_b64_tr_b16, and
+// two-deep register prefetch (see attn_tiles.h); the fp32 dtype uses plain
+// per-thread kernels with the same structure.
 #include <algorithm>
 
-#include "prism_internal.h"
+#include "attn_tiles.h"
 
 namespace prism {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// row of a 64-row operand feeding M-row m of M-tile mt (see attn_fwd.hip):
-// lane group g of the C layout then holds slots 32*(mt/2) + 8g + 4*(mt%2) + r
-__device__ __forceinline__ int slot_of(int mt, int m) {
-  return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
-}
-
-// pack the C-layout tiles (2*ks2, 2*ks2+1) into a bf16x8 B operand
-__device__ __forceinline__ bf16x8 pack_b(const f32x4& a, const f32x4& b) {
-  uint4 u;
-  u.x = (uint32_t)f32_to_bf16(a[0]) | ((uint32_t)f32_to_bf16(a[1]) << 16);
-  u.y = (uint32_t)f32_to_bf16(a[2]) | ((uint32_t)f32_to_bf16(a[3]) << 16);
-  u.z = (uint32_t)f32_to_bf16(b[0]) | ((uint32_t)f32_to_bf16(b[1]) << 16);
-  u.w = (uint32_t)f32_to_bf16(b[2]) | ((uint32_t)f32_to_bf16(b[3]) << 16);
-  return as_bf16x8(u);
-}
-
-// 64 gathered rows of a [., D] bf16 tensor into row-major (ld = D + 8) and
-// transposed (ld = 72) LDS copies; either destination may be null.
-template <int D>
-__device__ __forceinline__ void stage_rows(const uint16_t* __restrict__ src,
-                                           long long head, const int* rows,
-                                           uint16_t* rm, uint16_t* tr) {
-  const int tid = threadIdx.x;
-  if (rm) {
-#pragma unroll
-    for (int c = tid; c < 64 * (D / 8); c += 256) {
-      const int r = c / (D / 8), piece = c % (D / 8);
-      *reinterpret_cast<uint4*>(&rm[r * (D + 8) + piece * 8]) =
-          *reinterpret_cast<const uint4*>(src + (head + rows[r]) * D + piece * 8);
-    }
-  }
-  if (tr) {
-    for (int c = tid; c < (D / 8) * 16; c += 256) {
-      const int dc = c % (D / 8), rg = c / (D / 8);
-      uint4 r4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        r4[e] = *reinterpret_cast<const uint4*>(src + (head + rows[4 * rg + e]) * D + dc * 8);
-      const uint16_t* s0 = reinterpret_cast<const uint16_t*>(&r4[0]);
-      const uint16_t* s1 = reinterpret_cast<const uint16_t*>(&r4[1]);
-      const uint16_t* s2 = reinterpret_cast<const uint16_t*>(&r4[2]);
-      const uint16_t* s3 = reinterpret_cast<const uint16_t*>(&r4[3]);
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        uint2 pk;
-        pk.x = (uint32_t)s0[e8] | ((uint32_t)s1[e8] << 16);
-        pk.y = (uint32_t)s2[e8] | ((uint32_t)s3[e8] << 16);
-        *reinterpret_cast<uint2*>(&tr[(dc * 8 + e8) * 72 + 4 * rg]) = pk;
-      }
-    }
-  }
-}
 
 // ------------------------------------------------------------- helpers
 template <typename E>
@@ -144,224 +82,353 @@ __global__ void bitmap_build(const int32_t* __restrict__ counts,
 }
 
 // ------------------------------------------------------- dK / dV (bf16)
+// One workgroup per KV block, 4 waves = (kh, qh): KV rows 32*kh .. +31 (K, V
+// fragments in registers as B operands) against query rows 32*qh .. +31 of
+// every query block that selected this KV block.  The column bitmap is
+// compacted into an ascending list in LDS first; Q and dO tiles (plus lse,
+// D) are staged two blocks ahead through registers into swizzled LDS
+// tiles.  Q^T / dO^T fragments come from ds_read_b64_tr_b16.  The two qh
+// waves of a KV half sum their partial dK / dV at the end.
 template <int D>
-struct DkdvSmem {
-  uint16_t Q[64 * (D + 8)];
-  uint16_t Qt[D * 72];
-  uint16_t dO[64 * (D + 8)];
-  uint16_t dOt[D * 72];
-  float lse2[64];
-  float delta[64];
-  int rows[64];
-};
-
-template <int D>
-__global__ __launch_bounds__(256) void dkdv_bf16(
+__global__ __launch_bounds__(256, 1) void dkdv_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ perm, const uint32_t* __restrict__ bits,
-    int words, int Hh, int N, float scale, float* __restrict__ dk,
-    float* __restrict__ dv) {
-  constexpr int KS = D / 32, DT = D / 16, LD = D + 8;
-  __shared__ __align__(16) DkdvSmem<D> sm;
-  const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    int words, int Hh, int N, long long heads, float scale,
+    float* __restrict__ dk, float* __restrict__ dv) {
+  using namespace tiles;
+  using TL = Tile<D>;
+  constexpr int KS = D / 16, DT = D / 32;
+  extern __shared__ __align__(16) unsigned char dyn[];
+  unsigned char* sq = dyn;                              // Q tile
+  unsigned char* sdo = dyn + TL::kBytes;                // dO tile
+  float* s_lse = reinterpret_cast<float*>(dyn + 2 * TL::kBytes);   // [64]
+  float* s_dlt = s_lse + 64;                                       // [64]
+  int* s_cnt = reinterpret_cast<int*>(s_dlt + 64);                 // [8]
+  uint16_t* qlist = reinterpret_cast<uint16_t*>(s_cnt + 8);        // [Nb]
+
   const int Nb = N / 64;
+  long long bh;
+  int j;
+  if (!xcd_item(Nb, heads, bh, j)) return;
+  const int b = (int)(bh / Hh);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c16 = lane & 15;
-  const long long head = ((long long)b * Hh + h) * N;
+  const int kh = wave & 1, qh = wave >> 1;
+  const int c = lane & 31, hf = lane >> 5, j16 = lane & 15, grp = lane >> 4;
+  const long long head = bh * N;
   const int32_t* pb = perm + (long long)b * N;
   const float sl2 = scale * kLog2e;
 
-  const int kvrow = pb[64 * j + 16 * wave + c16];
+  // ascending list of the query blocks that selected block j: popcount
+  // prefix over the column's words, then each thread writes its set bits
+  const uint32_t* col = bits + (bh * Nb + j) * words;
+  if (tid == 0) s_cnt[0] = 0;
+  __syncthreads();
+  for (int w0 = 0; w0 < words; w0 += 256) {
+    const int w = w0 + tid;
+    const uint32_t word = w < words ? col[w] : 0u;
+    const int n = __popc(word);
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) s_cnt[1 + wave] = incl;
+    __syncthreads();
+    int pos = s_cnt[0] + incl - n;
+    for (int x = 0; x < wave; ++x) pos += s_cnt[1 + x];
+    uint32_t wd = word;
+    while (wd) {
+      qlist[pos++] = (uint16_t)(w * 32 + __ffs(wd) - 1);
+      wd &= wd - 1;
+    }
+    __syncthreads();
+    if (tid == 0) s_cnt[0] += (s_cnt[1] + s_cnt[2]) + (s_cnt[3] + s_cnt[4]);
+    __syncthreads();
+  }
+  const int cnt = s_cnt[0];
+
+  const int kvrow = pb[64 * j + 32 * kh + c];
   bf16x8 kreg[KS], vreg[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    kreg[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(k + (head + kvrow) * D + 32 * ks + 8 * g));
-    vreg[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(v + (head + kvrow) * D + 32 * ks + 8 * g));
+    kreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(k + (head + kvrow) * D + 16 * ks + 8 * hf));
+    vreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(v + (head + kvrow) * D + 16 * ks + 8 * hf));
   }
-  f32x4 dva[DT], dka[DT];
+  f32x16 dva[DT], dka[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
-    dva[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dka[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dva[t] = f32x16{};
+    dka[t] = f32x16{};
   }
-  const uint32_t* col = bits + (((long long)b * Hh + h) * Nb + j) * words;
+  // query row (within the block) of C-layout register r of this lane
+  int qslot[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    qslot[r] = 32 * qh + slot_of(8 * (r >> 2) + 4 * hf + (r & 3));
+  const int arow = 32 * qh + slot_of(c);      // Q / dO row of this lane's M-row
 
-  for (int w = 0; w < words; ++w) {
-    uint32_t word = col[w];
-    while (word) {
-      const int i = w * 32 + __ffs(word) - 1;
-      word &= word - 1;
-      __syncthreads();
-      if (tid < 64) {
-        const int r = pb[64 * i + tid];
-        sm.rows[tid] = r;
-        sm.lse2[tid] = lse[head + r] * kLog2e;
-        sm.delta[tid] = delta[head + r];
-      }
-      __syncthreads();
-      stage_rows<D>(q, head, sm.rows, sm.Q, sm.Qt);
-      stage_rows<D>(d_o, head, sm.rows, sm.dO, sm.dOt);
-      __syncthreads();
-
-      // S = Q K^T and dP = dO V^T: M = query slots, N = this wave's 16 kv
-      f32x4 s[4], dp[4];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int qr = slot_of(mt, c16);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(*reinterpret_cast<const uint4*>(&sm.Q[qr * LD + 32 * ks + 8 * g])),
-              kreg[ks], s[mt], 0, 0, 0);
-          dp[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(*reinterpret_cast<const uint4*>(&sm.dO[qr * LD + 32 * ks + 8 * g])),
-              vreg[ks], dp[mt], 0, 0, 0);
-        }
-      }
-      // P and dS; lane holds query slots slot_of(mt, 4g + r), kv c16
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qs = slot_of(mt, 4 * g + r);
-          const float p = exp2f(s[mt][r] * sl2 - sm.lse2[qs]);
-          s[mt][r] = p;
-          dp[mt][r] = p * (dp[mt][r] - sm.delta[qs]);
-        }
-      bf16x8 pB[2], dsB[2];
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        pB[ks2] = pack_b(s[2 * ks2], s[2 * ks2 + 1]);
-        dsB[ks2] = pack_b(dp[2 * ks2], dp[2 * ks2 + 1]);
-      }
-      // dV^T += dO^T P ; dK^T += Q^T dS   (M = d, N = kv, K = query slots)
-#pragma unroll
-      for (int mt = 0; mt < DT; ++mt) {
-        const int dr = 16 * mt + c16;
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-          dva[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(*reinterpret_cast<const uint4*>(&sm.dOt[dr * 72 + 32 * ks2 + 8 * g])),
-              pB[ks2], dva[mt], 0, 0, 0);
-          dka[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              as_bf16x8(*reinterpret_cast<const uint4*>(&sm.Qt[dr * 72 + 32 * ks2 + 8 * g])),
-              dsB[ks2], dka[mt], 0, 0, 0);
-        }
-      }
+  Stage<D> qA, oA, qB, oB;
+  float xA = 0.f, xB = 0.f;   // lse (tid < 64) or D (64 <= tid < 128) of a row
+  int rows_n[TL::kPerThread];
+  int xrow_n = 0;
+  int i_n = 0;
+  auto xload = [&](int blk) __attribute__((always_inline)) -> int {
+    return tid < 128 ? pb[64 * blk + (tid & 63)] : 0;
+  };
+  auto xval = [&](int row) __attribute__((always_inline)) -> float {
+    return tid < 64 ? lse[head + row] * kLog2e : (tid < 128 ? delta[head + row] : 0.f);
+  };
+  if (cnt > 0) {
+    int r0[TL::kPerThread];
+    stage_rows<D>(r0, pb, qlist[0], tid);
+    stage_load<D>(qA, q, head, r0, tid);
+    stage_load<D>(oA, d_o, head, r0, tid);
+    xA = xval(xload(qlist[0]));
+    if (cnt > 1) {
+      stage_rows<D>(r0, pb, qlist[1], tid);
+      stage_load<D>(qB, q, head, r0, tid);
+      stage_load<D>(oB, d_o, head, r0, tid);
+      xB = xval(xload(qlist[1]));
     }
+    if (cnt > 2) {
+      stage_rows<D>(rows_n, pb, qlist[2], tid);
+      xrow_n = xload(qlist[2]);
+    }
+    if (cnt > 3) i_n = qlist[3];
   }
-  // dV[kv c16][16mt + 4g + r]
+
+  auto compute_block = [&]() __attribute__((always_inline)) {
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32(lds_row8<D>(sq, arow, 2 * ks + hf), kreg[ks], s);
+      dp = mfma32(lds_row8<D>(sdo, arow, 2 * ks + hf), vreg[ks], dp);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(fmaf(s[r], sl2, -s_lse[qslot[r]]));
+      s[r] = p;
+      dp[r] = p * (dp[r] - s_dlt[qslot[r]]);
+    }
+    const bf16x8 p0 = pack8(s, 0), p1 = pack8(s, 1);
+    const bf16x8 g0 = pack8(dp, 0), g1 = pack8(dp, 1);
+#pragma unroll
+    for (int mt = 0; mt < DT; ++mt) {
+      const int d0 = 32 * mt + 16 * (grp & 1);
+      const int r0 = 32 * qh + 8 * (grp >> 1);
+      dva[mt] = mfma32(lds_tr8<D>(sdo, r0, d0, j16), p0, dva[mt]);
+      dva[mt] = mfma32(lds_tr8<D>(sdo, r0 + 16, d0, j16), p1, dva[mt]);
+      dka[mt] = mfma32(lds_tr8<D>(sq, r0, d0, j16), g0, dka[mt]);
+      dka[mt] = mfma32(lds_tr8<D>(sq, r0 + 16, d0, j16), g1, dka[mt]);
+    }
+  };
+
+#define PRISM_DKDV_STEP(T_, QS_, OS_, X_)                                   \
+  {                                                                         \
+    const int tt = (T_);                                                    \
+    __syncthreads();                                                        \
+    stage_store<D>(QS_, sq, tid);                                           \
+    stage_store<D>(OS_, sdo, tid);                                          \
+    if (tid < 64) s_lse[tid] = X_;                                          \
+    else if (tid < 128) s_dlt[tid - 64] = X_;                               \
+    __syncthreads();                                                        \
+    if (tt + 2 < cnt) {                                                     \
+      stage_load<D>(QS_, q, head, rows_n, tid);                             \
+      stage_load<D>(OS_, d_o, head, rows_n, tid);                           \
+      X_ = xval(xrow_n);                                                    \
+    }                                                                       \
+    if (tt + 3 < cnt) {                                                     \
+      stage_rows<D>(rows_n, pb, i_n, tid);                                  \
+      xrow_n = xload(i_n);                                                  \
+    }                                                                       \
+    if (tt + 4 < cnt) i_n = qlist[tt + 4];                                  \
+    compute_block();                                                        \
+  }
+
+  int t = 0;
+  for (; t + 1 < cnt; t += 2) {
+    PRISM_DKDV_STEP(t, qA, oA, xA)
+    PRISM_DKDV_STEP(t + 1, qB, oB, xB)
+  }
+  if (t < cnt) PRISM_DKDV_STEP(t, qA, oA, xA)
+#undef PRISM_DKDV_STEP
+
+  // sum the two qh partials: qh = 1 hands over through LDS, one tensor at a
+  // time (2 waves x 64 lanes x D/2 floats = 2 * TL::kBytes)
+  float* xch = reinterpret_cast<float*>(dyn);
   float* dvr = dv + (head + kvrow) * D;
   float* dkr = dk + (head + kvrow) * D;
+  for (int pass = 0; pass < 2; ++pass) {
+    f32x16* acc = pass == 0 ? dva : dka;
+    __syncthreads();
+    if (qh == 1) {
 #pragma unroll
-  for (int mt = 0; mt < DT; ++mt) {
-    *reinterpret_cast<float4*>(dvr + 16 * mt + 4 * g) =
-        make_float4(dva[mt][0], dva[mt][1], dva[mt][2], dva[mt][3]);
-    *reinterpret_cast<float4*>(dkr + 16 * mt + 4 * g) =
-        make_float4(dka[mt][0] * scale, dka[mt][1] * scale, dka[mt][2] * scale,
-                    dka[mt][3] * scale);
+      for (int mt = 0; mt < DT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          xch[((kh * 64 + lane) * DT + mt) * 16 + r] = acc[mt][r];
+    }
+    __syncthreads();
+    if (qh == 0) {
+      float* out = pass == 0 ? dvr : dkr;
+      const float f = pass == 0 ? 1.f : scale;
+#pragma unroll
+      for (int mt = 0; mt < DT; ++mt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float4 o4;
+          const float* x = &xch[((kh * 64 + lane) * DT + mt) * 16 + 4 * a];
+          o4.x = (acc[mt][4 * a + 0] + x[0]) * f;
+          o4.y = (acc[mt][4 * a + 1] + x[1]) * f;
+          o4.z = (acc[mt][4 * a + 2] + x[2]) * f;
+          o4.w = (acc[mt][4 * a + 3] + x[3]) * f;
+          *reinterpret_cast<float4*>(out + 32 * mt + 8 * a + 4 * hf) = o4;
+        }
+    }
   }
 }
 
 // ------------------------------------------------------------ dQ (bf16)
+// One workgroup per query block, waves (qh, kh) as in the forward: S^T and
+// dP^T per 32x32 tile, dQ^T += K^T dS^T with K^T fragments from
+// ds_read_b64_tr_b16; K and V staged two blocks ahead.
 template <int D>
-struct DqSmem {
-  uint16_t K[64 * (D + 8)];
-  uint16_t Kt[D * 72];
-  uint16_t V[64 * (D + 8)];
-  int rows[64];
-};
-
-template <int D>
-__global__ __launch_bounds__(256) void dq_bf16(
+__global__ __launch_bounds__(256, 1) void dq_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ kv_idx, int capacity, int Hh, int N,
-    float scale, float* __restrict__ dq) {
-  constexpr int KS = D / 32, DT = D / 16, LD = D + 8;
-  __shared__ __align__(16) DqSmem<D> sm;
-  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    long long heads, float scale, float* __restrict__ dq) {
+  using namespace tiles;
+  using TL = Tile<D>;
+  constexpr int KS = D / 16, DT = D / 32;
+  __shared__ __align__(16) unsigned char smem[2 * TL::kBytes];
+  unsigned char* sk = smem;
+  unsigned char* sv = smem + TL::kBytes;
+
   const int Nb = N / 64;
+  long long bh;
+  int i;
+  if (!xcd_item(Nb, heads, bh, i)) return;
+  const int b = (int)(bh / Hh);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = lane >> 4, c16 = lane & 15;
-  const long long head = ((long long)b * Hh + h) * N;
+  const int qh = wave & 1, kh = wave >> 1;
+  const int c = lane & 31, hf = lane >> 5, j16 = lane & 15, grp = lane >> 4;
+  const long long head = bh * N;
   const int32_t* pb = perm + (long long)b * N;
   const float sl2 = scale * kLog2e;
 
-  const int qrow = pb[64 * i + 16 * wave + c16];
+  const int qrow = pb[64 * i + 32 * qh + c];
   bf16x8 qreg[KS], doreg[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qreg[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(q + (head + qrow) * D + 32 * ks + 8 * g));
-    doreg[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(d_o + (head + qrow) * D + 32 * ks + 8 * g));
+    qreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(q + (head + qrow) * D + 16 * ks + 8 * hf));
+    doreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(d_o + (head + qrow) * D + 16 * ks + 8 * hf));
   }
   const float lse2 = lse[head + qrow] * kLog2e;
   const float dlt = delta[head + qrow];
-  f32x4 dqa[DT];
+  f32x16 dqa[DT];
 #pragma unroll
-  for (int t = 0; t < DT; ++t) dqa[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < DT; ++t) dqa[t] = f32x16{};
+  const int arow = 32 * kh + slot_of(c);
 
-  const long long rowid = ((long long)b * Hh + h) * Nb + i;
+  const long long rowid = bh * Nb + i;
   const int cnt = counts[rowid];
   const int32_t* lst = kv_idx + rowid * (long long)capacity;
-  for (int t = 0; t < cnt; ++t) {
-    const int j = lst[t];
-    __syncthreads();
-    if (tid < 64) sm.rows[tid] = pb[64 * j + tid];
-    __syncthreads();
-    stage_rows<D>(k, head, sm.rows, sm.K, sm.Kt);
-    stage_rows<D>(v, head, sm.rows, sm.V, nullptr);
-    __syncthreads();
-    // S^T = K Q^T, dP^T = V dO^T   (M = kv slots, N = this wave's queries)
-    f32x4 s[4], dp[4];
+
+  Stage<D> kA, vA, kB, vB;
+  int rows_n[TL::kPerThread];
+  int j_n = 0;
+  {
+    int r0[TL::kPerThread];
+    stage_rows<D>(r0, pb, lst[0], tid);
+    stage_load<D>(kA, k, head, r0, tid);
+    stage_load<D>(vA, v, head, r0, tid);
+    if (cnt > 1) {
+      stage_rows<D>(r0, pb, lst[1], tid);
+      stage_load<D>(kB, k, head, r0, tid);
+      stage_load<D>(vB, v, head, r0, tid);
+    }
+    if (cnt > 2) stage_rows<D>(rows_n, pb, lst[2], tid);
+    if (cnt > 3) j_n = lst[3];
+  }
+
+  auto compute_block = [&]() __attribute__((always_inline)) {
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int kr = slot_of(mt, c16);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(&sm.K[kr * LD + 32 * ks + 8 * g])),
-            qreg[ks], s[mt], 0, 0, 0);
-        dp[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(&sm.V[kr * LD + 32 * ks + 8 * g])),
-            doreg[ks], dp[mt], 0, 0, 0);
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32(lds_row8<D>(sk, arow, 2 * ks + hf), qreg[ks], s);
+      dp = mfma32(lds_row8<D>(sv, arow, 2 * ks + hf), doreg[ks], dp);
     }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = exp2f(s[mt][r] * sl2 - lse2);
-        dp[mt][r] = p * (dp[mt][r] - dlt);
-      }
-    bf16x8 dsB[2];
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) dsB[ks2] = pack_b(dp[2 * ks2], dp[2 * ks2 + 1]);
-    // dQ^T += K^T dS^T  (M = d, N = queries, K = kv slots)
+    for (int r = 0; r < 16; ++r) {
+      const float p = exp2_fast(fmaf(s[r], sl2, -lse2));
+      dp[r] = p * (dp[r] - dlt);
+    }
+    const bf16x8 g0 = pack8(dp, 0), g1 = pack8(dp, 1);
 #pragma unroll
     for (int mt = 0; mt < DT; ++mt) {
-      const int dr = 16 * mt + c16;
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-        dqa[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            as_bf16x8(*reinterpret_cast<const uint4*>(&sm.Kt[dr * 72 + 32 * ks2 + 8 * g])),
-            dsB[ks2], dqa[mt], 0, 0, 0);
+      const int d0 = 32 * mt + 16 * (grp & 1);
+      const int r0 = 32 * kh + 8 * (grp >> 1);
+      dqa[mt] = mfma32(lds_tr8<D>(sk, r0, d0, j16), g0, dqa[mt]);
+      dqa[mt] = mfma32(lds_tr8<D>(sk, r0 + 16, d0, j16), g1, dqa[mt]);
     }
+  };
+
+#define PRISM_DQ_STEP(T_, KS_, VS_)                                         \
+  {                                                                         \
+    const int tt = (T_);                                                    \
+    __syncthreads();                                                        \
+    stage_store<D>(KS_, sk, tid);                                           \
+    stage_store<D>(VS_, sv, tid);                                           \
+    __syncthreads();                                                        \
+    if (tt + 2 < cnt) {                                                     \
+      stage_load<D>(KS_, k, head, rows_n, tid);                             \
+      stage_load<D>(VS_, v, head, rows_n, tid);                             \
+    }                                                                       \
+    if (tt + 3 < cnt) stage_rows<D>(rows_n, pb, j_n, tid);                  \
+    if (tt + 4 < cnt) j_n = lst[tt + 4];                                    \
+    compute_block();                                                        \
   }
-  float* dqr = dq + (head + qrow) * D;
+
+  int t = 0;
+  for (; t + 1 < cnt; t += 2) {
+    PRISM_DQ_STEP(t, kA, vA)
+    PRISM_DQ_STEP(t + 1, kB, vB)
+  }
+  if (t < cnt) PRISM_DQ_STEP(t, kA, vA)
+#undef PRISM_DQ_STEP
+
+  // sum the two kh partials
+  __syncthreads();
+  float* xch = reinterpret_cast<float*>(smem);
+  if (kh == 1) {
 #pragma unroll
-  for (int mt = 0; mt < DT; ++mt)
-    *reinterpret_cast<float4*>(dqr + 16 * mt + 4 * g) =
-        make_float4(dqa[mt][0] * scale, dqa[mt][1] * scale, dqa[mt][2] * scale,
-                    dqa[mt][3] * scale);
+    for (int mt = 0; mt < DT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        xch[((qh * 64 + lane) * DT + mt) * 16 + r] = dqa[mt][r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    float* dqr = dq + (head + qrow) * D;
+#pragma unroll
+    for (int mt = 0; mt < DT; ++mt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float* x = &xch[((qh * 64 + lane) * DT + mt) * 16 + 4 * a];
+        float4 o4;
+        o4.x = (dqa[mt][4 * a + 0] + x[0]) * scale;
+        o4.y = (dqa[mt][4 * a + 1] + x[1]) * scale;
+        o4.z = (dqa[mt][4 * a + 2] + x[2]) * scale;
+        o4.w = (dqa[mt][4 * a + 3] + x[3]) * scale;
+        *reinterpret_cast<float4*>(dqr + 32 * mt + 8 * a + 4 * hf) = o4;
+      }
+  }
 }
 
 // ------------------------------------------------------ fp32 reference
@@ -487,13 +554,18 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
 
   dim3 grid(Nb, Hh, B);
   if (dtype == PRISM_BF16) {
-    PRISM_LAUNCH("dkdv_bf16", dkdv_bf16<D>, grid, dim3(256), 0, stream, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o,
-                       lse, delta, perm, bits, words, Hh, N, scale, dk, dv);
+    const long long heads = (long long)B * Hh;
+    const dim3 g1(tiles::xcd_grid(Nb, heads));
+    const size_t dyn = 2 * tiles::Tile<D>::kBytes + 128 * sizeof(float) +
+                       8 * sizeof(int) + (size_t)Nb * sizeof(uint16_t);
+    PRISM_LAUNCH("dkdv_bf16", dkdv_bf16<D>, g1, dim3(256), dyn, stream,
+                 (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                 (const uint16_t*)d_o, lse, delta, perm, bits, words, Hh, N, heads,
+                 scale, dk, dv);
     if ((st = check_launch("dkdv_bf16")) != PRISM_OK) return st;
-    PRISM_LAUNCH("dq_bf16", dq_bf16<D>, grid, dim3(256), 0, stream, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o,
-                       lse, delta, perm, counts, kv_idx, capacity, Hh, N, scale, dq);
+    PRISM_LAUNCH("dq_bf16", dq_bf16<D>, g1, dim3(256), 0, stream, (const uint16_t*)q,
+                 (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o,
+                 lse, delta, perm, counts, kv_idx, capacity, Hh, N, heads, scale, dq);
     return check_launch("dq_bf16");
   }
   PRISM_LAUNCH("dkdv_f32", dkdv_f32<D>, grid, dim3(64), 0, stream, (const float*)q,

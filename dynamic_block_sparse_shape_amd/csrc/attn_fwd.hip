@@ -113,26 +113,27 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       s = mfma32(lds_row8<D>(sk, krow, 2 * ks + hf), qreg[ks], s);
-    float mx = -INFINITY;
+    // online softmax in the log2 domain (scale > 0, so the max of the raw
+    // scores is the max of the scaled ones)
+    float mx = s[0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] *= scale_log2;
-      mx = fmaxf(mx, s[r]);
-    }
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
+    const float m_new = fmaxf(m_run, mx * scale_log2);
+    const float alpha = exp2_fast(m_run - m_new);
     float rs = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[r] = exp2f(s[r] - m_new);
+      s[r] = exp2_fast(fmaf(s[r], scale_log2, -m_new));
       rs += s[r];
     }
     rs += __shfl_xor(rs, 32, 64);
     l_run = l_run * alpha + rs;
     m_run = m_new;
+    if (__any(alpha != 1.f)) {      // the running max moved for some query
 #pragma unroll
-    for (int t2 = 0; t2 < DT; ++t2) oacc[t2] *= alpha;
+      for (int t2 = 0; t2 < DT; ++t2) oacc[t2] *= alpha;
+    }
     const bf16x8 p0 = pack8(s, 0), p1 = pack8(s, 1);
     // O^T (d x 32 q) += V_half^T P^T
 #pragma unroll
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
   if (kh == 0) {
     const float m2 = sm_m[qh][c], l2 = sm_l[qh][c];
     const float m = fmaxf(m_run, m2);
-    const float a1 = exp2f(m_run - m), a2 = exp2f(m2 - m);
+    const float a1 = exp2_fast(m_run - m), a2 = exp2_fast(m2 - m);
     const float l = l_run * a1 + l2 * a2;
     const float inv_l = 1.f / l;
     uint16_t* orow = o + (head + qrow) * D;
@@ -187,8 +188,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
                       xo[((qh * 64 + lane) * DT + mt) * 16 + r] * a2) * inv_l;
         }
         uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16(vals[0]) | ((uint32_t)f32_to_bf16(vals[1]) << 16);
-        pk.y = (uint32_t)f32_to_bf16(vals[2]) | ((uint32_t)f32_to_bf16(vals[3]) << 16);
+        pk.x = cvt2(vals[0], vals[1]);
+        pk.y = cvt2(vals[2], vals[3]);
         *reinterpret_cast<uint2*>(orow + 32 * mt + 8 * a + 4 * hf) = pk;
       }
     if (hf == 0) lse[head + qrow] = (m + log2f(l)) * kLn2;

@@ -26,6 +26,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -138,13 +140,23 @@ __device__ __forceinline__ void stage_rows(int* rows,
     rows[t] = pb[64 * j + Tile<D>::row_of(tid, t)];
 }
 
+// Two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t cvt2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// 2^x with the hardware v_exp_f32 (inputs here are <= 0 or -inf).
+__device__ __forceinline__ float exp2_fast(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
 // Pack C-layout registers 8s .. 8s+7 into a bf16 B operand.
 __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int s) {
   u32x4 u;
-  u.x = (uint32_t)f32_to_bf16(c[8 * s + 0]) | ((uint32_t)f32_to_bf16(c[8 * s + 1]) << 16);
-  u.y = (uint32_t)f32_to_bf16(c[8 * s + 2]) | ((uint32_t)f32_to_bf16(c[8 * s + 3]) << 16);
-  u.z = (uint32_t)f32_to_bf16(c[8 * s + 4]) | ((uint32_t)f32_to_bf16(c[8 * s + 5]) << 16);
-  u.w = (uint32_t)f32_to_bf16(c[8 * s + 6]) | ((uint32_t)f32_to_bf16(c[8 * s + 7]) << 16);
+  u.x = cvt2(c[8 * s + 0], c[8 * s + 1]);
+  u.y = cvt2(c[8 * s + 2], c[8 * s + 3]);
+  u.z = cvt2(c[8 * s + 4], c[8 * s + 5]);
+  u.w = cvt2(c[8 * s + 6], c[8 * s + 7]);
   return as_bf16x8(u);
 }
 
