@@ -83,14 +83,14 @@ __global__ void bitmap_build(const int32_t* __restrict__ counts,
 
 // ------------------------------------------------------- dK / dV (bf16)
 // One workgroup per KV block, 4 waves = (kh, qh): KV rows 32*kh .. +31 (K, V
-// fragments in registers as B operands) against query rows 32*qh .. +31 of
+// tiles resident in LDS, B operands) against query rows 32*qh .. +31 of
 // every query block that selected this KV block.  The column bitmap is
 // compacted into an ascending list in LDS first; Q and dO tiles (plus lse,
-// D) are staged two blocks ahead through registers into swizzled LDS
+// D) are staged one block ahead through registers into swizzled LDS
 // tiles.  Q^T / dO^T fragments come from ds_read_b64_tr_b16.  The two qh
 // waves of a KV half sum their partial dK / dV at the end.
 template <int D>
-__global__ __launch_bounds__(256, 1) void dkdv_bf16(
+__global__ __launch_bounds__(256, 2) void dkdv_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta,
@@ -103,7 +103,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16(
   extern __shared__ __align__(16) unsigned char dyn[];
   unsigned char* sq = dyn;                              // Q tile
   unsigned char* sdo = dyn + TL::kBytes;                // dO tile
-  float* s_lse = reinterpret_cast<float*>(dyn + 2 * TL::kBytes);   // [64]
+  unsigned char* skt = dyn + 2 * TL::kBytes;            // this block's K
+  unsigned char* svt = dyn + 3 * TL::kBytes;            // this block's V
+  float* s_lse = reinterpret_cast<float*>(dyn + 4 * TL::kBytes);   // [64]
   float* s_dlt = s_lse + 64;                                       // [64]
   int* s_cnt = reinterpret_cast<int*>(s_dlt + 64);                 // [8]
   uint16_t* qlist = reinterpret_cast<uint16_t*>(s_cnt + 8);        // [Nb]
@@ -151,11 +153,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16(
   const int cnt = s_cnt[0];
 
   const int kvrow = pb[64 * j + 32 * kh + c];
-  bf16x8 kreg[KS], vreg[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(k + (head + kvrow) * D + 16 * ks + 8 * hf));
-    vreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(v + (head + kvrow) * D + 16 * ks + 8 * hf));
+  const int brow = 32 * kh + c;               // K / V row of this lane's column
+  {
+    // this KV block's K and V stay in LDS for the whole kernel (B operands)
+    int r0[TL::kPerThread];
+    Stage<D> ks0, vs0;
+    stage_rows<D>(r0, pb, j, tid);
+    stage_load<D>(ks0, k, head, r0, tid);
+    stage_load<D>(vs0, v, head, r0, tid);
+    stage_store<D>(ks0, skt, tid);
+    stage_store<D>(vs0, svt, tid);
   }
   f32x16 dva[DT], dka[DT];
 #pragma unroll
@@ -163,55 +170,71 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16(
     dva[t] = f32x16{};
     dka[t] = f32x16{};
   }
-  // query row (within the block) of C-layout register r of this lane
-  int qslot[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r)
-    qslot[r] = 32 * qh + slot_of(8 * (r >> 2) + 4 * hf + (r & 3));
+  // C-layout register 4a + b of this lane holds query row
+  // qbase(a) + b, qbase(a) = 32 qh + 16 (a / 2) + 8 hf + 4 (a % 2)
   const int arow = 32 * qh + slot_of(c);      // Q / dO row of this lane's M-row
 
-  Stage<D> qA, oA, qB, oB;
-  float xA = 0.f, xB = 0.f;   // lse (tid < 64) or D (64 <= tid < 128) of a row
+  // one query block staged ahead in registers; past the end of the list the
+  // last block is re-fetched (branch-free loop body)
+  Stage<D> qS, oS;
+  float xS = 0.f;             // lse * log2(e) (tid < 64) or D (64 <= tid < 128)
   int rows_n[TL::kPerThread];
   int xrow_n = 0;
   int i_n = 0;
+  const int last = cnt - 1;
   auto xload = [&](int blk) __attribute__((always_inline)) -> int {
-    return tid < 128 ? pb[64 * blk + (tid & 63)] : 0;
+    return pb[64 * blk + (tid & 63)];
   };
   auto xval = [&](int row) __attribute__((always_inline)) -> float {
-    return tid < 64 ? lse[head + row] * kLog2e : (tid < 128 ? delta[head + row] : 0.f);
+    return tid < 64 ? lse[head + row] * kLog2e : delta[head + row];
   };
   if (cnt > 0) {
     int r0[TL::kPerThread];
     stage_rows<D>(r0, pb, qlist[0], tid);
-    stage_load<D>(qA, q, head, r0, tid);
-    stage_load<D>(oA, d_o, head, r0, tid);
-    xA = xval(xload(qlist[0]));
-    if (cnt > 1) {
-      stage_rows<D>(r0, pb, qlist[1], tid);
-      stage_load<D>(qB, q, head, r0, tid);
-      stage_load<D>(oB, d_o, head, r0, tid);
-      xB = xval(xload(qlist[1]));
-    }
-    if (cnt > 2) {
-      stage_rows<D>(rows_n, pb, qlist[2], tid);
-      xrow_n = xload(qlist[2]);
-    }
-    if (cnt > 3) i_n = qlist[3];
+    stage_load<D>(qS, q, head, r0, tid);
+    stage_load<D>(oS, d_o, head, r0, tid);
+    xS = xval(xload(qlist[0]));
+    stage_rows<D>(rows_n, pb, qlist[min(1, last)], tid);
+    xrow_n = xload(qlist[min(1, last)]);
+    i_n = qlist[min(2, last)];
   }
 
-  auto compute_block = [&]() __attribute__((always_inline)) {
+  for (int t = 0; t < cnt; ++t) {
+    __syncthreads();
+    stage_store<D>(qS, sq, tid);
+    stage_store<D>(oS, sdo, tid);
+    if (tid < 64) s_lse[tid] = xS;
+    else if (tid < 128) s_dlt[tid - 64] = xS;
+    __syncthreads();
+    stage_load<D>(qS, q, head, rows_n, tid);
+    stage_load<D>(oS, d_o, head, rows_n, tid);
+    xS = xval(xrow_n);
+    stage_rows<D>(rows_n, pb, i_n, tid);
+    xrow_n = xload(i_n);
+    i_n = qlist[min(t + 3, last)];
+
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32(lds_row8<D>(sq, arow, 2 * ks + hf), kreg[ks], s);
-      dp = mfma32(lds_row8<D>(sdo, arow, 2 * ks + hf), vreg[ks], dp);
+      s = mfma32(lds_row8<D>(sq, arow, 2 * ks + hf),
+                 lds_row8<D>(skt, brow, 2 * ks + hf), s);
+      dp = mfma32(lds_row8<D>(sdo, arow, 2 * ks + hf),
+                  lds_row8<D>(svt, brow, 2 * ks + hf), dp);
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = exp2_fast(fmaf(s[r], sl2, -s_lse[qslot[r]]));
-      s[r] = p;
-      dp[r] = p * (dp[r] - s_dlt[qslot[r]]);
+    for (int a = 0; a < 4; ++a) {
+      const int qb = 32 * qh + 16 * (a >> 1) + 8 * hf + 4 * (a & 1);
+      const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[qb]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&s_dlt[qb]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int r = 4 * a + bb;
+        const float p = exp2_fast(fmaf(s[r], sl2, -lv[bb]));
+        s[r] = p;
+        dp[r] = p * (dp[r] - dv4[bb]);
+      }
     }
     const bf16x8 p0 = pack8(s, 0), p1 = pack8(s, 1);
     const bf16x8 g0 = pack8(dp, 0), g1 = pack8(dp, 1);
@@ -224,37 +247,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16(
       dka[mt] = mfma32(lds_tr8<D>(sq, r0, d0, j16), g0, dka[mt]);
       dka[mt] = mfma32(lds_tr8<D>(sq, r0 + 16, d0, j16), g1, dka[mt]);
     }
-  };
-
-#define PRISM_DKDV_STEP(T_, QS_, OS_, X_)                                   \
-  {                                                                         \
-    const int tt = (T_);                                                    \
-    __syncthreads();                                                        \
-    stage_store<D>(QS_, sq, tid);                                           \
-    stage_store<D>(OS_, sdo, tid);                                          \
-    if (tid < 64) s_lse[tid] = X_;                                          \
-    else if (tid < 128) s_dlt[tid - 64] = X_;                               \
-    __syncthreads();                                                        \
-    if (tt + 2 < cnt) {                                                     \
-      stage_load<D>(QS_, q, head, rows_n, tid);                             \
-      stage_load<D>(OS_, d_o, head, rows_n, tid);                           \
-      X_ = xval(xrow_n);                                                    \
-    }                                                                       \
-    if (tt + 3 < cnt) {                                                     \
-      stage_rows<D>(rows_n, pb, i_n, tid);                                  \
-      xrow_n = xload(i_n);                                                  \
-    }                                                                       \
-    if (tt + 4 < cnt) i_n = qlist[tt + 4];                                  \
-    compute_block();                                                        \
   }
-
-  int t = 0;
-  for (; t + 1 < cnt; t += 2) {
-    PRISM_DKDV_STEP(t, qA, oA, xA)
-    PRISM_DKDV_STEP(t + 1, qB, oB, xB)
-  }
-  if (t < cnt) PRISM_DKDV_STEP(t, qA, oA, xA)
-#undef PRISM_DKDV_STEP
 
   // sum the two qh partials: qh = 1 hands over through LDS, one tensor at a
   // time (2 waves x 64 lanes x D/2 floats = 2 * TL::kBytes)
@@ -294,9 +287,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16(
 // ------------------------------------------------------------ dQ (bf16)
 // One workgroup per query block, waves (qh, kh) as in the forward: S^T and
 // dP^T per 32x32 tile, dQ^T += K^T dS^T with K^T fragments from
-// ds_read_b64_tr_b16; K and V staged two blocks ahead.
+// ds_read_b64_tr_b16; K and V staged one block ahead.
 template <int D>
-__global__ __launch_bounds__(256, 1) void dq_bf16(
+__global__ __launch_bounds__(256, 2) void dq_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta,
@@ -340,24 +333,32 @@ __global__ __launch_bounds__(256, 1) void dq_bf16(
   const int cnt = counts[rowid];
   const int32_t* lst = kv_idx + rowid * (long long)capacity;
 
-  Stage<D> kA, vA, kB, vB;
+  // one block staged ahead in registers (keeps the kernel at 2 waves/SIMD);
+  // past the end of the list the last block is re-fetched, keeping the loop
+  // body free of branches (exact wait counters)
+  Stage<D> kS, vS;
   int rows_n[TL::kPerThread];
-  int j_n = 0;
+  const int last = cnt - 1;
+  int j_n;
   {
     int r0[TL::kPerThread];
     stage_rows<D>(r0, pb, lst[0], tid);
-    stage_load<D>(kA, k, head, r0, tid);
-    stage_load<D>(vA, v, head, r0, tid);
-    if (cnt > 1) {
-      stage_rows<D>(r0, pb, lst[1], tid);
-      stage_load<D>(kB, k, head, r0, tid);
-      stage_load<D>(vB, v, head, r0, tid);
-    }
-    if (cnt > 2) stage_rows<D>(rows_n, pb, lst[2], tid);
-    if (cnt > 3) j_n = lst[3];
+    stage_load<D>(kS, k, head, r0, tid);
+    stage_load<D>(vS, v, head, r0, tid);
+    stage_rows<D>(rows_n, pb, lst[min(1, last)], tid);
+    j_n = lst[min(2, last)];
   }
 
-  auto compute_block = [&]() __attribute__((always_inline)) {
+  for (int t = 0; t < cnt; ++t) {
+    __syncthreads();
+    stage_store<D>(kS, sk, tid);
+    stage_store<D>(vS, sv, tid);
+    __syncthreads();
+    stage_load<D>(kS, k, head, rows_n, tid);
+    stage_load<D>(vS, v, head, rows_n, tid);
+    stage_rows<D>(rows_n, pb, j_n, tid);
+    j_n = lst[min(t + 3, last)];
+
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -377,31 +378,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16(
       dqa[mt] = mfma32(lds_tr8<D>(sk, r0, d0, j16), g0, dqa[mt]);
       dqa[mt] = mfma32(lds_tr8<D>(sk, r0 + 16, d0, j16), g1, dqa[mt]);
     }
-  };
-
-#define PRISM_DQ_STEP(T_, KS_, VS_)                                         \
-  {                                                                         \
-    const int tt = (T_);                                                    \
-    __syncthreads();                                                        \
-    stage_store<D>(KS_, sk, tid);                                           \
-    stage_store<D>(VS_, sv, tid);                                           \
-    __syncthreads();                                                        \
-    if (tt + 2 < cnt) {                                                     \
-      stage_load<D>(KS_, k, head, rows_n, tid);                             \
-      stage_load<D>(VS_, v, head, rows_n, tid);                             \
-    }                                                                       \
-    if (tt + 3 < cnt) stage_rows<D>(rows_n, pb, j_n, tid);                  \
-    if (tt + 4 < cnt) j_n = lst[tt + 4];                                    \
-    compute_block();                                                        \
   }
-
-  int t = 0;
-  for (; t + 1 < cnt; t += 2) {
-    PRISM_DQ_STEP(t, kA, vA)
-    PRISM_DQ_STEP(t + 1, kB, vB)
-  }
-  if (t < cnt) PRISM_DQ_STEP(t, kA, vA)
-#undef PRISM_DQ_STEP
 
   // sum the two kh partials
   __syncthreads();
@@ -556,7 +533,7 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
   if (dtype == PRISM_BF16) {
     const long long heads = (long long)B * Hh;
     const dim3 g1(tiles::xcd_grid(Nb, heads));
-    const size_t dyn = 2 * tiles::Tile<D>::kBytes + 128 * sizeof(float) +
+    const size_t dyn = 4 * tiles::Tile<D>::kBytes + 128 * sizeof(float) +
                        8 * sizeof(int) + (size_t)Nb * sizeof(uint16_t);
     PRISM_LAUNCH("dkdv_bf16", dkdv_bf16<D>, g1, dim3(256), dyn, stream,
                  (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,

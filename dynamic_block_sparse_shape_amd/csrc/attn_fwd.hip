@@ -74,19 +74,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
   Stage<D> kA, vA, kB, vB;
   int rows_n[TL::kPerThread];
   int j_n = 0;
-  // prologue: blocks 0 and 1 in flight, rows of block 2, id of block 3
+  // prologue: blocks 0 and 1 in flight, rows of block 2, id of block 3.
+  // Past the end of the list the last block is re-fetched instead, so the
+  // loop body has no branches and the compiler's wait counters stay exact.
+  const int last = cnt - 1;
   {
     int r0[TL::kPerThread];
     stage_rows<D>(r0, pb, lst[0], tid);
     stage_load<D>(kA, k, head, r0, tid);
     stage_load<D>(vA, v, head, r0, tid);
-    if (cnt > 1) {
-      stage_rows<D>(r0, pb, lst[1], tid);
-      stage_load<D>(kB, k, head, r0, tid);
-      stage_load<D>(vB, v, head, r0, tid);
-    }
-    if (cnt > 2) stage_rows<D>(rows_n, pb, lst[2], tid);
-    if (cnt > 3) j_n = lst[3];
+    stage_rows<D>(r0, pb, lst[min(1, last)], tid);
+    stage_load<D>(kB, k, head, r0, tid);
+    stage_load<D>(vB, v, head, r0, tid);
+    stage_rows<D>(rows_n, pb, lst[min(2, last)], tid);
+    j_n = lst[min(3, last)];
   }
 
 // One KV block: publish the staged block t to LDS, refill the stage with
@@ -98,12 +99,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
     stage_store<D>(KS_, sk, tid);                                           \
     stage_store<D>(VS_, sv, tid);                                           \
     __syncthreads();                                                        \
-    if (tt + 2 < cnt) {                                                     \
-      stage_load<D>(KS_, k, head, rows_n, tid);                             \
-      stage_load<D>(VS_, v, head, rows_n, tid);                             \
-    }                                                                       \
-    if (tt + 3 < cnt) stage_rows<D>(rows_n, pb, j_n, tid);                  \
-    if (tt + 4 < cnt) j_n = lst[tt + 4];                                    \
+    stage_load<D>(KS_, k, head, rows_n, tid);                               \
+    stage_load<D>(VS_, v, head, rows_n, tid);                               \
+    stage_rows<D>(rows_n, pb, j_n, tid);                                    \
+    j_n = lst[min(tt + 4, last)];                                           \
     compute_block();                                                        \
   }
 
