@@ -156,11 +156,11 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
   const int brow = 32 * kh + c;               // K / V row of this lane's column
   {
     // this KV block's K and V stay in LDS for the whole kernel (B operands)
-    int r0[TL::kPerThread];
+    uint32_t o0[TL::kPerThread];
     Stage<D> ks0, vs0;
-    stage_rows<D>(r0, pb, j, tid);
-    stage_load<D>(ks0, k, head, r0, tid);
-    stage_load<D>(vs0, v, head, r0, tid);
+    stage_offsets<D>(o0, pb, j, tid);
+    stage_load<D>(ks0, head_rsrc<D>(k, head, N), o0);
+    stage_load<D>(vs0, head_rsrc<D>(v, head, N), o0);
     stage_store<D>(ks0, skt, tid);
     stage_store<D>(vs0, svt, tid);
   }
@@ -178,7 +178,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
   // last block is re-fetched (branch-free loop body)
   Stage<D> qS, oS;
   float xS = 0.f;             // lse * log2(e) (tid < 64) or D (64 <= tid < 128)
-  int rows_n[TL::kPerThread];
+  const __amdgpu_buffer_rsrc_t rq = head_rsrc<D>(q, head, N);
+  const __amdgpu_buffer_rsrc_t ro = head_rsrc<D>(d_o, head, N);
+  uint32_t offs_n[TL::kPerThread];
   int xrow_n = 0;
   int i_n = 0;
   const int last = cnt - 1;
@@ -189,12 +191,12 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
     return tid < 64 ? lse[head + row] * kLog2e : delta[head + row];
   };
   if (cnt > 0) {
-    int r0[TL::kPerThread];
-    stage_rows<D>(r0, pb, qlist[0], tid);
-    stage_load<D>(qS, q, head, r0, tid);
-    stage_load<D>(oS, d_o, head, r0, tid);
+    uint32_t o0[TL::kPerThread];
+    stage_offsets<D>(o0, pb, qlist[0], tid);
+    stage_load<D>(qS, rq, o0);
+    stage_load<D>(oS, ro, o0);
     xS = xval(xload(qlist[0]));
-    stage_rows<D>(rows_n, pb, qlist[min(1, last)], tid);
+    stage_offsets<D>(offs_n, pb, qlist[min(1, last)], tid);
     xrow_n = xload(qlist[min(1, last)]);
     i_n = qlist[min(2, last)];
   }
@@ -206,10 +208,10 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
     if (tid < 64) s_lse[tid] = xS;
     else if (tid < 128) s_dlt[tid - 64] = xS;
     __syncthreads();
-    stage_load<D>(qS, q, head, rows_n, tid);
-    stage_load<D>(oS, d_o, head, rows_n, tid);
+    stage_load<D>(qS, rq, offs_n);
+    stage_load<D>(oS, ro, offs_n);
     xS = xval(xrow_n);
-    stage_rows<D>(rows_n, pb, i_n, tid);
+    stage_offsets<D>(offs_n, pb, i_n, tid);
     xrow_n = xload(i_n);
     i_n = qlist[min(t + 3, last)];
 
@@ -337,15 +339,17 @@ __global__ __launch_bounds__(256, 2) void dq_bf16(
   // past the end of the list the last block is re-fetched, keeping the loop
   // body free of branches (exact wait counters)
   Stage<D> kS, vS;
-  int rows_n[TL::kPerThread];
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(k, head, N);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(v, head, N);
+  uint32_t offs_n[TL::kPerThread];
   const int last = cnt - 1;
   int j_n;
   {
-    int r0[TL::kPerThread];
-    stage_rows<D>(r0, pb, lst[0], tid);
-    stage_load<D>(kS, k, head, r0, tid);
-    stage_load<D>(vS, v, head, r0, tid);
-    stage_rows<D>(rows_n, pb, lst[min(1, last)], tid);
+    uint32_t o0[TL::kPerThread];
+    stage_offsets<D>(o0, pb, lst[0], tid);
+    stage_load<D>(kS, rk, o0);
+    stage_load<D>(vS, rv, o0);
+    stage_offsets<D>(offs_n, pb, lst[min(1, last)], tid);
     j_n = lst[min(2, last)];
   }
 
@@ -354,9 +358,9 @@ __global__ __launch_bounds__(256, 2) void dq_bf16(
     stage_store<D>(kS, sk, tid);
     stage_store<D>(vS, sv, tid);
     __syncthreads();
-    stage_load<D>(kS, k, head, rows_n, tid);
-    stage_load<D>(vS, v, head, rows_n, tid);
-    stage_rows<D>(rows_n, pb, j_n, tid);
+    stage_load<D>(kS, rk, offs_n);
+    stage_load<D>(vS, rv, offs_n);
+    stage_offsets<D>(offs_n, pb, j_n, tid);
     j_n = lst[min(t + 3, last)];
 
     f32x16 s = f32x16{}, dp = f32x16{};

@@ -38,10 +38,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
   using TL = Tile<D>;
   constexpr int KS = D / 16;     // k-steps of S^T = K Q^T
   constexpr int DT = D / 32;     // 32-row d tiles of O^T
-  __shared__ __align__(16) unsigned char smem[2 * TL::kBytes];
+  // two LDS buffers (K and V of one block each): block t+1 is published into
+  // one while block t is read from the other -- one barrier per block
+  __shared__ __align__(16) unsigned char smem[4 * TL::kBytes];
   __shared__ float sm_m[2][32], sm_l[2][32];
-  unsigned char* sk = smem;
-  unsigned char* sv = smem + TL::kBytes;
 
   const int Nb = N / 64;
   long long bh;
@@ -72,53 +72,67 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
   const int krow = 32 * kh + slot_of(c);   // K row feeding this lane's M-row
 
   Stage<D> kA, vA, kB, vB;
-  int rows_n[TL::kPerThread];
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(k, head, N);
+  const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(v, head, N);
+  uint32_t offs_n[TL::kPerThread];
   int j_n = 0;
-  // prologue: blocks 0 and 1 in flight, rows of block 2, id of block 3.
-  // Past the end of the list the last block is re-fetched instead, so the
-  // loop body has no branches and the compiler's wait counters stay exact.
+  // prologue: block 0 published to buffer 0, block 1 staged, block 2 in
+  // flight, offsets of block 3, id of block 4.  Past the end of the list the
+  // last block is re-fetched, so the loop body has no branches and the
+  // compiler's wait counters stay exact.
   const int last = cnt - 1;
   {
-    int r0[TL::kPerThread];
-    stage_rows<D>(r0, pb, lst[0], tid);
-    stage_load<D>(kA, k, head, r0, tid);
-    stage_load<D>(vA, v, head, r0, tid);
-    stage_rows<D>(r0, pb, lst[min(1, last)], tid);
-    stage_load<D>(kB, k, head, r0, tid);
-    stage_load<D>(vB, v, head, r0, tid);
-    stage_rows<D>(rows_n, pb, lst[min(2, last)], tid);
-    j_n = lst[min(3, last)];
+    uint32_t o0[TL::kPerThread];
+    stage_offsets<D>(o0, pb, lst[0], tid);
+    stage_load<D>(kA, rk, o0);
+    stage_load<D>(vA, rv, o0);
+    stage_offsets<D>(o0, pb, lst[min(1, last)], tid);
+    stage_load<D>(kB, rk, o0);
+    stage_load<D>(vB, rv, o0);
+    stage_store<D>(kA, smem, tid);
+    stage_store<D>(vA, smem + TL::kBytes, tid);
+    stage_offsets<D>(o0, pb, lst[min(2, last)], tid);
+    stage_load<D>(kA, rk, o0);
+    stage_load<D>(vA, rv, o0);
+    stage_offsets<D>(offs_n, pb, lst[min(3, last)], tid);
+    j_n = lst[min(4, last)];
   }
 
-// One KV block: publish the staged block t to LDS, refill the stage with
-// block t+2, advance the row / id prefetch, then compute on LDS.
-#define PRISM_FWD_STEP(T_, KS_, VS_)                                        \
+// One KV block t (in buffer t % 2): publish staged block t+1 into the other
+// buffer, refill that stage with block t+3, advance the row / id prefetch,
+// compute block t.
+#define PRISM_FWD_STEP(T_, BUF_, KS_, VS_)                                  \
   {                                                                         \
     const int tt = (T_);                                                    \
     __syncthreads();                                                        \
-    stage_store<D>(KS_, sk, tid);                                           \
-    stage_store<D>(VS_, sv, tid);                                           \
-    __syncthreads();                                                        \
-    stage_load<D>(KS_, k, head, rows_n, tid);                               \
-    stage_load<D>(VS_, v, head, rows_n, tid);                               \
-    stage_rows<D>(rows_n, pb, j_n, tid);                                    \
-    j_n = lst[min(tt + 4, last)];                                           \
-    compute_block();                                                        \
+    stage_store<D>(KS_, smem + (1 - (BUF_)) * 2 * TL::kBytes, tid);         \
+    stage_store<D>(VS_, smem + (1 - (BUF_)) * 2 * TL::kBytes + TL::kBytes,  \
+                   tid);                                                    \
+    stage_load<D>(KS_, rk, offs_n);                                         \
+    stage_load<D>(VS_, rv, offs_n);                                         \
+    stage_offsets<D>(offs_n, pb, j_n, tid);                                 \
+    j_n = lst[min(tt + 5, last)];                                           \
+    compute_block(smem + (BUF_) * 2 * TL::kBytes,                           \
+                  smem + (BUF_) * 2 * TL::kBytes + TL::kBytes);             \
   }
 
-  auto compute_block = [&]() __attribute__((always_inline)) {
+  auto compute_block = [&](const unsigned char* sk, const unsigned char* sv)
+                           __attribute__((always_inline)) {
     // S^T (32 kv x 32 q) = K_half Q_half^T
     f32x16 s = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       s = mfma32(lds_row8<D>(sk, krow, 2 * ks + hf), qreg[ks], s);
     // online softmax in the log2 domain (scale > 0, so the max of the raw
-    // scores is the max of the scaled ones)
+    // scores is the max of the scaled ones).  The exponent reference m_run
+    // only moves when a block's max exceeds it by more than 8: until then
+    // the probabilities stay <= 2^8 (exact range in fp32 and bf16) and the
+    // accumulator needs no rescale.
     float mx = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * scale_log2);
+    mx = xor32_max(mx) * scale_log2;
+    const float m_new = mx > m_run + 8.f ? mx : m_run;
     const float alpha = exp2_fast(m_run - m_new);
     float rs = 0.f;
 #pragma unroll
@@ -126,10 +140,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
       s[r] = exp2_fast(fmaf(s[r], scale_log2, -m_new));
       rs += s[r];
     }
-    rs += __shfl_xor(rs, 32, 64);
+    rs = xor32_sum(rs);
     l_run = l_run * alpha + rs;
     m_run = m_new;
-    if (__any(alpha != 1.f)) {      // the running max moved for some query
+    if (__any(alpha != 1.f)) {      // the reference moved for some query
 #pragma unroll
       for (int t2 = 0; t2 < DT; ++t2) oacc[t2] *= alpha;
     }
@@ -144,12 +158,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
     }
   };
 
+  // stage B holds block t+1 at even t, stage A at odd t
   int t = 0;
   for (; t + 1 < cnt; t += 2) {
-    PRISM_FWD_STEP(t, kA, vA)
-    PRISM_FWD_STEP(t + 1, kB, vB)
+    PRISM_FWD_STEP(t, 0, kB, vB)
+    PRISM_FWD_STEP(t + 1, 1, kA, vA)
   }
-  if (t < cnt) PRISM_FWD_STEP(t, kA, vA)
+  if (t < cnt) PRISM_FWD_STEP(t, 0, kB, vB)
 #undef PRISM_FWD_STEP
 
   // merge the two KV halves: waves kh = 1 hand over (m, l, O) through LDS

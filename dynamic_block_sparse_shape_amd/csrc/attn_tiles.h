@@ -101,23 +101,41 @@ __device__ __forceinline__ bf16x8 lds_tr8(const unsigned char* tile, int r0,
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Global -> register staging of one 64-row tile (rows gathered through
-// row indices held by the thread).
+// Global -> register staging of one 64-row tile.  Rows are gathered with
+// buffer loads: one resource per (tensor, head) and 32-bit byte offsets that
+// the K and V (or Q and dO) tiles of a block share.
 template <int D>
 struct Stage {
   u32x4 v[Tile<D>::kPerThread];   // clang vectors: promotable to registers
 };
 
+// Buffer resource over one head's [N, D] bf16 rows (loads past the end
+// return zeros instead of faulting).
 template <int D>
-__device__ __forceinline__ void stage_load(Stage<D>& s,
-                                           const uint16_t* __restrict__ src,
-                                           long long head, const int* rows,
-                                           int tid) {
-  const int p = Tile<D>::piece_of(tid);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(
+    const uint16_t* base, long long head_row0, int N) {
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(base + head_row0 * D), (short)0, N * D * 2,
+      0x00020000);
+}
+
+// Byte offsets (within the head) of this thread's pieces of block j.
+template <int D>
+__device__ __forceinline__ void stage_offsets(uint32_t* offs,
+                                              const int32_t* __restrict__ pb,
+                                              int j, int tid) {
+  const uint32_t p16 = (uint32_t)Tile<D>::piece_of(tid) * 16u;
 #pragma unroll
   for (int t = 0; t < Tile<D>::kPerThread; ++t)
-    s.v[t] = *reinterpret_cast<const u32x4*>(
-        src + (head + rows[t]) * D + p * 8);
+    offs[t] = (uint32_t)pb[64 * j + Tile<D>::row_of(tid, t)] * (uint32_t)(D * 2) + p16;
+}
+
+template <int D>
+__device__ __forceinline__ void stage_load(Stage<D>& s, __amdgpu_buffer_rsrc_t r,
+                                           const uint32_t* offs) {
+#pragma unroll
+  for (int t = 0; t < Tile<D>::kPerThread; ++t)
+    s.v[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offs[t], 0, 0));
 }
 
 template <int D>
@@ -130,19 +148,22 @@ __device__ __forceinline__ void stage_store(const Stage<D>& s,
         s.v[t];
 }
 
-// Row indices this thread needs to stage block j (perm[64 j + row]).
-template <int D>
-__device__ __forceinline__ void stage_rows(int* rows,
-                                           const int32_t* __restrict__ pb,
-                                           int j, int tid) {
-#pragma unroll
-  for (int t = 0; t < Tile<D>::kPerThread; ++t)
-    rows[t] = pb[64 * j + Tile<D>::row_of(tid, t)];
-}
-
 // Two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t cvt2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Combine a value with the one held by lane l ^ 32: v_permlane32_swap
+// (gfx950) hands every lane its partner's value without touching LDS.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // 2^x with the hardware v_exp_f32 (inputs here are <= 0 or -inf).
