@@ -7,20 +7,26 @@
 // The mass is the running fp64 sum in that order.
 //
 // One workgroup per proxy row; the row (<= 8192 fp64) lives in registers.
-//  1. Radix refinement on the fp64 bit patterns (non-negative doubles order
-//     like unsigned integers), 8 bits per pass, with per-bucket counts and
-//     approximate masses in LDS, narrows the candidates to the smallest
-//     prefix of buckets whose count reaches max(k, 1) and whose mass exceeds
-//     the threshold by a safety margin far above any summation-order error.
-//     That set is a prefix of the sorted order and holds the answer.
-//  2. The <= 2048 candidates are bitonic-sorted in LDS by (score desc,
-//     index asc).
-//  3. A parallel scan of the sorted scores locates where the mass crosses
-//     the threshold; only when the crossing is within the scan's rounding
-//     bound of a tie does one lane redo the running sum one block at a time,
-//     so the count always equals that of the sequential definition.
-//  4. The first c sorted blocks are marked in an LDS bitmap and written in
-//     ascending index order with ballot / popcount compaction.
+//  1. Windowed radix refinement on the fp64 bit patterns (non-negative
+//     doubles order like unsigned integers).  Each pass buckets the keys of
+//     the current band [lo, hi] by 255 - min(255, (hi >> s) - (key >> s)):
+//     the first pass (s = 48: 16 buckets per octave, 16 octaves below the
+//     row maximum) already spreads a softmax row well; later passes take 8
+//     more bits.  Per-bucket counts and approximate masses in LDS locate the
+//     bucket where the count reaches max(k, 1) and the mass exceeds the
+//     threshold by a safety margin far above any summation-order error;
+//     everything above it is selected, the search continues inside it.
+//  2. Fast path: once that band holds <= 64 keys and the mass above it is
+//     clearly below the threshold, one wave sorts the band by (score desc,
+//     index asc) in registers and a scan locates where the mass crosses the
+//     threshold.  The count equals the sequential definition's whenever the
+//     crossing is not within rounding reach of the threshold.
+//  3. Otherwise the whole candidate prefix (<= 2048 keys) is bitonic-sorted
+//     in LDS and scanned; only when the crossing is within the scan's
+//     rounding bound of a tie does one lane redo the running sum one block
+//     at a time.
+//  4. The selection is kept as an LDS bitmap and written in ascending index
+//     order (one bitmap word per thread, prefix sum of popcounts).
 // Rows whose candidates do not fit the sort buffer, or whose whole mass
 // lies within rounding of the threshold, take an exact slow path that
 // extracts blocks one at a time in sorted order.
@@ -32,6 +38,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSortCap = 2048;
+constexpr int kBand = 64;          // band size for the one-wave fast path
 constexpr double kMassMargin = 1e-11;  // >> (n + 64) * 2^-53 for n <= 8192
 
 struct SelShared {
@@ -39,8 +46,9 @@ struct SelShared {
   double hmass[256];
   unsigned long long ckey[kSortCap];
   int cidx[kSortCap];
-  unsigned bits[8192 / 32];
+  unsigned bits[kThreads];   // 8192 bits: one word per thread
   double wsum[kWaves];
+  unsigned long long wmax[kWaves];
   int wcnt[kWaves];
   int s_int[8];
   double s_dbl[8];
@@ -59,7 +67,7 @@ __device__ __forceinline__ double wave_sum(double v) {
 }
 
 template <int NPT>
-__global__ __launch_bounds__(kThreads) void select_rows(
+__global__ __launch_bounds__(kThreads, 4) void select_rows(
     const double* __restrict__ proxy, int Nb, int top_k, double tau,
     int32_t* __restrict__ counts, int32_t* __restrict__ kv_idx,
     int capacity) {
@@ -72,6 +80,7 @@ __global__ __launch_bounds__(kThreads) void select_rows(
 
   unsigned long long key[NPT];
   double total = 0.0;
+  unsigned long long kmax = 0ull;
 #pragma unroll
   for (int e = 0; e < NPT; ++e) {
     const int j = tid + e * kThreads;
@@ -79,44 +88,101 @@ __global__ __launch_bounds__(kThreads) void select_rows(
     p = p > 0.0 ? p : 0.0;  // scores are probabilities; clamp -0 / NaN
     key[e] = j < Nb ? (unsigned long long)__double_as_longlong(p) : 0ull;
     total += p;
+    kmax = key[e] > kmax ? key[e] : kmax;
   }
   total = wave_sum(total);
-  if (lane == 0) sh.wsum[wave] = total;
-  for (int w = tid; w < (Nb + 31) / 32; w += kThreads) sh.bits[w] = 0u;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const unsigned long long o = __shfl_xor(kmax, off, 64);
+    kmax = o > kmax ? o : kmax;
+  }
+  if (lane == 0) {
+    sh.wsum[wave] = total;
+    sh.wmax[wave] = kmax;
+  }
+  sh.bits[tid] = 0u;
   __syncthreads();
   total = (sh.wsum[0] + sh.wsum[1]) + (sh.wsum[2] + sh.wsum[3]);
+  {
+    const unsigned long long m01 = sh.wmax[0] > sh.wmax[1] ? sh.wmax[0] : sh.wmax[1];
+    const unsigned long long m23 = sh.wmax[2] > sh.wmax[3] ? sh.wmax[2] : sh.wmax[3];
+    kmax = m01 > m23 ? m01 : m23;
+  }
 
   const int kk = min(top_k, Nb);
   const int kneed = max(kk, 1);
-  // mode: 0 = all blocks, 1 = sort candidates, 2 = exact slow path
+  // mode: 0 = all blocks, 1 = sort candidates, 2 = exact slow path,
+  //       3 = selection decided by the band fast path
   int mode;
   unsigned long long theta = 0ull;
   int ncand = 0;
+  int c = 0;
   if (kk >= Nb || total < tau - kMassMargin) {
     mode = 0;
   } else if (total < tau + kMassMargin) {
     mode = 2;
   } else {
-    // ---------------------------------------------- radix refinement
-    unsigned long long prefix = 0ull, mask = 0ull;
-    int cnt_above = 0;
+    // ------------------------------------- windowed radix refinement
+    // The band [lo, hi] holds the crossing; keys above hi are selected
+    // (cnt_above, mass_above) and keys below lo are not.  Each pass
+    // histograms the window [wlo, whi] at the band's top, 256 buckets of
+    // 2^s keys, counts keys in (whi, hi] without atomics and ignores keys
+    // below the window.  The first window is a quarter octave around the row
+    // mean at 1/1024 octave per bucket: a near-flat softmax row keeps most
+    // of its keys there and spreads them over many buckets.
+    unsigned long long lo = 0ull, hi = kmax;
+    unsigned long long whi;
+    {
+      const double anchor = total / (double)Nb * 1.0905077326652577;  // 2^(1/8)
+      const unsigned long long ka = (unsigned long long)__double_as_longlong(anchor);
+      whi = ka < hi ? ka : hi;
+    }
+    int s = 42;
+    int cnt_above = 0, cnt_ge_lo = Nb, band_cnt = Nb;
     double mass_above = 0.0;
     mode = 2;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int pass = 0; pass < 64; ++pass) {
       sh.hcnt[tid] = 0;
       sh.hmass[tid] = 0.0;
       __syncthreads();
+      const unsigned long long top = whi >> s;
+      const unsigned long long wraw = top >= 255ull ? ((top - 255ull) << s) : 0ull;
+      const unsigned long long wlo = wraw > lo ? wraw : lo;
+      const bool split = whi < hi;     // keys in (whi, hi] are counted apart
+      int acnt = 0;
+      double amass = 0.0;
 #pragma unroll
       for (int e = 0; e < NPT; ++e) {
         const int j = tid + e * kThreads;
-        if (j < Nb && (key[e] & mask) == prefix) {
-          const int dg = (int)((key[e] >> shift) & 0xffull);
-          atomicAdd(&sh.hcnt[dg], 1);
-          atomicAdd(&sh.hmass[dg], __longlong_as_double((long long)key[e]));
+        if (j < Nb && key[e] >= wlo && key[e] <= hi) {
+          const double x = __longlong_as_double((long long)key[e]);
+          if (key[e] > whi) {
+            ++acnt;
+            amass += x;
+          } else {
+            const int dg = 255 - (int)(top - (key[e] >> s));
+            atomicAdd(&sh.hcnt[dg], 1);
+            atomicAdd(&sh.hmass[dg], x);
+          }
+        }
+      }
+      if (split) {
+        amass = wave_sum(amass);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acnt += __shfl_xor(acnt, off, 64);
+        if (lane == 0) {
+          sh.wcnt[wave] = acnt;
+          sh.wsum[wave] = amass;
         }
       }
       __syncthreads();
       if (wave == 0) {
+        int c0 = cnt_above;
+        double m0 = mass_above;
+        if (split) {
+          c0 += (sh.wcnt[0] + sh.wcnt[1]) + (sh.wcnt[2] + sh.wcnt[3]);
+          m0 += (sh.wsum[0] + sh.wsum[1]) + (sh.wsum[2] + sh.wsum[3]);
+        }
         // lane l owns digits 255-4l .. 252-4l (descending)
         int c4[4];
         double m4[4];
@@ -141,66 +207,195 @@ __global__ __launch_bounds__(kThreads) void select_rows(
             im += om;
           }
         }
-        int cc = cnt_above + ic - lc;
-        double cm = mass_above + (im - lm);
-        int hit = -1;
-        int hit_cum = 0;
+        int cc = c0 + ic - lc;
+        double cm = m0 + (im - lm);
+        int hit = -1, hit_cum = 0, hit_above = 0;
+        double hit_mabove = 0.0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          const int cb = cc;
+          const double mb = cm;
           cc += c4[q];
           cm += m4[q];
           if (hit < 0 && c4[q] > 0 && cc >= kneed && cm >= tau + kMassMargin) {
             hit = 255 - 4 * lane - q;
             hit_cum = cc;
+            hit_above = cb;
+            hit_mabove = mb;
           }
         }
         const unsigned long long bal = __ballot(hit >= 0);
         const int first = bal ? __ffsll((long long)bal) - 1 : -1;
-        if (lane == first) {
-          sh.s_int[0] = hit;
-          sh.s_int[1] = hit_cum;
+        if (c0 >= kneed && m0 >= tau + kMassMargin) {
+          // the crossing lies above the window, in (whi, hi]
+          if (lane == 0) {
+            sh.s_int[0] = 256;
+            sh.s_int[1] = c0;
+          }
+        } else if (first >= 0) {
+          if (lane == first) {
+            sh.s_int[0] = hit;
+            sh.s_int[1] = hit_cum;
+            sh.s_int[2] = hit_above;
+            sh.s_dbl[0] = hit_mabove;
+          }
+        } else if (lane == 63) {
+          // below the window: everything down to wlo is selected
+          sh.s_int[0] = -1;
+          sh.s_int[2] = cc;
+          sh.s_dbl[0] = cm;
         }
-        if (first < 0 && lane == 0) sh.s_int[0] = -1;
       }
       __syncthreads();
       const int D = sh.s_int[0];
-      const int cum = sh.s_int[1];
-      __syncthreads();
-      if (D < 0) {  // cannot happen when total >= tau + margin; be safe
-        mode = 2;
-        break;
-      }
-      if (cum <= kSortCap) {
-        theta = prefix | ((unsigned long long)D << shift);
-        ncand = cum;
-        mode = 1;
-        break;
-      }
-      if (shift == 0) {  // more than kSortCap identical keys
-        mode = 2;
-        break;
-      }
-      // refine inside bucket D: everything above it is in for good
-      if (tid == 0) {
-        int ca = 0;
-        double ma = 0.0;
-        for (int dg = 255; dg > D; --dg) {
-          ca += sh.hcnt[dg];
-          ma += sh.hmass[dg];
+      if (D == 256) {
+        lo = whi + 1ull;
+        cnt_ge_lo = sh.s_int[1];
+        whi = hi;
+        s = 48;
+      } else if (D >= 0) {
+        const unsigned long long base = top - (unsigned long long)(255 - D);
+        const unsigned long long nlo = base << s;
+        const unsigned long long nhi = nlo + ((1ull << s) - 1ull);
+        lo = nlo > lo ? nlo : lo;
+        hi = nhi < whi ? nhi : whi;
+        whi = hi;
+        cnt_ge_lo = sh.s_int[1];
+        cnt_above = sh.s_int[2];
+        mass_above = sh.s_dbl[0];
+      } else {
+        if (wlo <= lo) break;   // cannot happen when total >= tau + margin
+        cnt_above = sh.s_int[2];
+        mass_above = sh.s_dbl[0];
+        // next window starts at the largest key left below this one
+        const unsigned long long cap = wlo - 1ull;
+        unsigned long long mk = 0ull;
+#pragma unroll
+        for (int e = 0; e < NPT; ++e) {
+          const int j = tid + e * kThreads;
+          if (j < Nb && key[e] >= lo && key[e] <= cap && key[e] > mk) mk = key[e];
         }
-        sh.s_int[2] = ca;
-        sh.s_dbl[0] = ma;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          const unsigned long long o = __shfl_xor(mk, off, 64);
+          mk = o > mk ? o : mk;
+        }
+        if (lane == 0) sh.wmax[wave] = mk;
+        __syncthreads();
+        const unsigned long long m01 = sh.wmax[0] > sh.wmax[1] ? sh.wmax[0] : sh.wmax[1];
+        const unsigned long long m23 = sh.wmax[2] > sh.wmax[3] ? sh.wmax[2] : sh.wmax[3];
+        hi = m01 > m23 ? m01 : m23;
+        whi = hi;
+        s = 48;
+      }
+      band_cnt = cnt_ge_lo - cnt_above;
+      // mass above the band clearly below the threshold (the crossing lies
+      // in the band) or clearly above it (the count k decides)
+      const bool clear = mass_above < tau - kMassMargin ||
+                         mass_above > tau + kMassMargin;
+      if (!clear) break;
+      if (band_cnt <= kBand) {
+        mode = 3;
+        break;
+      }
+      if (D >= 0 && D < 256) {
+        if (s == 0) break;   // a run of identical keys
+        s = s > 8 ? s - 8 : 0;
+      }
+    }
+    if (mode == 3) {
+      // ------------------------------------------------ band fast path
+      if (tid == 0) sh.s_int[3] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < NPT; ++e) {
+        const int j = tid + e * kThreads;
+        if (j < Nb && key[e] >= lo && key[e] <= hi) {
+          const int pos = atomicAdd(&sh.s_int[3], 1);
+          if (pos < kBand) {
+            sh.ckey[pos] = key[e];
+            sh.cidx[pos] = j;
+          }
+        }
       }
       __syncthreads();
-      cnt_above += sh.s_int[2];
-      mass_above += sh.s_dbl[0];
-      prefix |= (unsigned long long)D << shift;
-      mask |= 0xffull << shift;
+      if (wave == 0) {
+        unsigned long long bk = lane < band_cnt ? sh.ckey[lane] : 0ull;
+        int bi = lane < band_cnt ? sh.cidx[lane] : 0x7fffffff;
+        // bitonic sort over the 64 lanes: lane order = (score desc, index asc)
+        for (int size = 2; size <= 64; size <<= 1) {
+          for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const unsigned long long ok = __shfl_xor(bk, stride, 64);
+            const int oi = __shfl_xor(bi, stride, 64);
+            // ascending runs (lane & size == 0) put the element that comes
+            // first in the lower lane of each pair, descending runs in the
+            // upper one
+            const bool want_first = ((lane & stride) == 0) == ((lane & size) == 0);
+            const bool take = want_first ? before(ok, oi, bk, bi) : before(bk, bi, ok, oi);
+            if (take) {
+              bk = ok;
+              bi = oi;
+            }
+          }
+        }
+        const double x = __longlong_as_double((long long)bk);
+        double incl = x;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const double o = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += o;
+        }
+        bool ok;
+        int m;
+        if (mass_above > tau + kMassMargin) {
+          // the mass was reached above the band: only the count k is open
+          ok = true;
+          m = cnt_above;
+        } else {
+          const double run = mass_above + incl;
+          const double prev = run - x;
+          const unsigned long long crossed = __ballot(lane < band_cnt && run >= tau);
+          const int t = crossed ? __ffsll((long long)crossed) - 1 : -1;
+          const double run_t = __shfl(run, t < 0 ? 0 : t, 64);
+          const double prev_t = __shfl(prev, t < 0 ? 0 : t, 64);
+          ok = t >= 0 && run_t - tau > kMassMargin && tau - prev_t > kMassMargin;
+          m = cnt_above + t + 1;
+        }
+        int take_n = 0;
+        if (ok) {
+          const int cc = min(Nb, max(kk, m));
+          take_n = cc - cnt_above;
+          if (lane == 0) sh.s_int[4] = cc;
+        }
+        if (lane == 0) sh.s_int[5] = ok ? 1 : 0;
+        if (ok && lane < take_n && lane < band_cnt)
+          atomicOr(&sh.bits[bi >> 5], 1u << (bi & 31));
+      }
       __syncthreads();
+      if (sh.s_int[5]) {
+        c = sh.s_int[4];
+        // every key above the band is selected: one bitmap word per
+        // (slot, wave, half-wave), written from a ballot
+#pragma unroll
+        for (int e = 0; e < NPT; ++e) {
+          const int j = tid + e * kThreads;
+          const unsigned long long bal = __ballot(j < Nb && key[e] > hi);
+          const int w = (e * kThreads + wave * 64) >> 5;
+          if (lane == 0 && (unsigned)bal) atomicOr(&sh.bits[w], (unsigned)bal);
+          if (lane == 32 && (unsigned)(bal >> 32))
+            atomicOr(&sh.bits[w + 1], (unsigned)(bal >> 32));
+        }
+      } else {
+        mode = 2;
+      }
+    }
+    if (mode == 2 && cnt_ge_lo <= kSortCap) {
+      theta = lo;
+      ncand = cnt_ge_lo;
+      mode = 1;
     }
   }
 
-  int c = 0;
   if (mode == 0) {
     c = Nb;
     for (int w = tid; w < (Nb + 31) / 32; w += kThreads) {
@@ -363,19 +558,26 @@ __global__ __launch_bounds__(kThreads) void select_rows(
   __syncthreads();
 
   // ------------------------------------------ ascending compaction
-  int base = 0;
-  for (int j0 = 0; j0 < Nb; j0 += kThreads) {
-    const int j = j0 + tid;
-    const bool f = j < Nb && ((sh.bits[j >> 5] >> (j & 31)) & 1u);
-    const unsigned long long bal = __ballot(f);
-    const int before_in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) sh.wcnt[wave] = __popcll(bal);
+  // thread w owns bitmap word w (Nb <= 8192 = 32 * kThreads)
+  {
+    const int words = (Nb + 31) / 32;
+    const unsigned wd = tid < words ? sh.bits[tid] : 0u;
+    const int n = __popc(wd);
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) sh.wcnt[wave] = incl;
     __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += sh.wcnt[w];
-    if (f) out[off + before_in_wave] = j;
-    base += (sh.wcnt[0] + sh.wcnt[1]) + (sh.wcnt[2] + sh.wcnt[3]);
-    __syncthreads();
+    int pos = incl - n;
+    for (int w = 0; w < wave; ++w) pos += sh.wcnt[w];
+    unsigned rest = wd;
+    while (rest) {
+      out[pos++] = tid * 32 + __ffs(rest) - 1;
+      rest &= rest - 1u;
+    }
   }
   if (tid == 0) counts[row] = c;
 }
@@ -386,18 +588,19 @@ prism_status launch_select(const double* proxy, int B, int Hh, int Nb,
                            int top_k, double tau, int32_t* counts,
                            int32_t* kv_idx, int capacity, hipStream_t stream) {
   const unsigned rows = (unsigned)((long long)B * Hh * Nb);
-  if (Nb <= 4 * kThreads)
-    PRISM_LAUNCH("select_rows", select_rows<4>, dim3(rows), dim3(kThreads), 0, stream,
-                       proxy, Nb, top_k, tau, counts, kv_idx, capacity);
-  else if (Nb <= 8 * kThreads)
-    PRISM_LAUNCH("select_rows", select_rows<8>, dim3(rows), dim3(kThreads), 0, stream,
-                       proxy, Nb, top_k, tau, counts, kv_idx, capacity);
-  else if (Nb <= 16 * kThreads)
-    PRISM_LAUNCH("select_rows", select_rows<16>, dim3(rows), dim3(kThreads), 0, stream,
-                       proxy, Nb, top_k, tau, counts, kv_idx, capacity);
-  else
-    PRISM_LAUNCH("select_rows", select_rows<32>, dim3(rows), dim3(kThreads), 0, stream,
-                       proxy, Nb, top_k, tau, counts, kv_idx, capacity);
+  // keys per thread: the smallest instantiated multiple of 4 covering the row
+  const int per = (Nb + kThreads - 1) / kThreads;
+#define PRISM_SELECT(NPT_)                                                     \
+  PRISM_LAUNCH("select_rows", select_rows<NPT_>, dim3(rows), dim3(kThreads), 0, \
+               stream, proxy, Nb, top_k, tau, counts, kv_idx, capacity)
+  if (per <= 4) PRISM_SELECT(4);
+  else if (per <= 8) PRISM_SELECT(8);
+  else if (per <= 12) PRISM_SELECT(12);
+  else if (per <= 16) PRISM_SELECT(16);
+  else if (per <= 20) PRISM_SELECT(20);
+  else if (per <= 24) PRISM_SELECT(24);
+  else PRISM_SELECT(32);
+#undef PRISM_SELECT
   return check_launch("select_rows");
 }
 
