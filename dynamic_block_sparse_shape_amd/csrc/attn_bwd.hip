@@ -177,7 +177,11 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
   // one query block staged ahead in registers; past the end of the list the
   // last block is re-fetched (branch-free loop body)
   Stage<D> qS, oS;
-  float xS = 0.f;             // lse * log2(e) (tid < 64) or D (64 <= tid < 128)
+  // lse (tid < 64) or D (64 <= tid < 128) of one row of the staged block;
+  // scaled to log2 units when it is published
+  float xS = 0.f;
+  const float* xsrc = (tid < 64 ? lse : delta) + head;
+  const float xscale = tid < 64 ? kLog2e : 1.f;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc<D>(q, head, N);
   const __amdgpu_buffer_rsrc_t ro = head_rsrc<D>(d_o, head, N);
   uint32_t offs_n[TL::kPerThread];
@@ -187,15 +191,12 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
   auto xload = [&](int blk) __attribute__((always_inline)) -> int {
     return pb[64 * blk + (tid & 63)];
   };
-  auto xval = [&](int row) __attribute__((always_inline)) -> float {
-    return tid < 64 ? lse[head + row] * kLog2e : delta[head + row];
-  };
   if (cnt > 0) {
     uint32_t o0[TL::kPerThread];
     stage_offsets<D>(o0, pb, qlist[0], tid);
     stage_load<D>(qS, rq, o0);
     stage_load<D>(oS, ro, o0);
-    xS = xval(xload(qlist[0]));
+    xS = xsrc[xload(qlist[0])];
     stage_offsets<D>(offs_n, pb, qlist[min(1, last)], tid);
     xrow_n = xload(qlist[min(1, last)]);
     i_n = qlist[min(2, last)];
@@ -205,14 +206,16 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
     __syncthreads();
     stage_store<D>(qS, sq, tid);
     stage_store<D>(oS, sdo, tid);
-    if (tid < 64) s_lse[tid] = xS;
-    else if (tid < 128) s_dlt[tid - 64] = xS;
+    if (tid < 128) s_lse[tid] = xS * xscale;     // s_dlt follows s_lse
     __syncthreads();
+    // small loads first (block t+1's lse / D, block t+2's rows), then the
+    // tiles of block t+1: the small ones retire without waiting for those
+    const float xS_n = xsrc[xrow_n];
+    int rows_n[TL::kPerThread];
+    stage_rows<D>(rows_n, pb, i_n, tid);
+    const int xrow_nn = xload(i_n);
     stage_load<D>(qS, rq, offs_n);
     stage_load<D>(oS, ro, offs_n);
-    xS = xval(xrow_n);
-    stage_offsets<D>(offs_n, pb, i_n, tid);
-    xrow_n = xload(i_n);
     i_n = qlist[min(t + 3, last)];
 
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -249,6 +252,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
       dka[mt] = mfma32(lds_tr8<D>(sq, r0, d0, j16), g0, dka[mt]);
       dka[mt] = mfma32(lds_tr8<D>(sq, r0 + 16, d0, j16), g1, dka[mt]);
     }
+    xS = xS_n;
+    xrow_n = xrow_nn;
+    rows_to_offsets<D>(offs_n, rows_n, tid);
   }
 
   // sum the two qh partials: qh = 1 hands over through LDS, one tensor at a
@@ -358,9 +364,12 @@ __global__ __launch_bounds__(256, 2) void dq_bf16(
     stage_store<D>(kS, sk, tid);
     stage_store<D>(vS, sv, tid);
     __syncthreads();
+    int rows_n[TL::kPerThread];
+    stage_rows<D>(rows_n, pb, j_n, tid);
+    pin_order();
     stage_load<D>(kS, rk, offs_n);
     stage_load<D>(vS, rv, offs_n);
-    stage_offsets<D>(offs_n, pb, j_n, tid);
+    pin_order();
     j_n = lst[min(t + 3, last)];
 
     f32x16 s = f32x16{}, dp = f32x16{};
@@ -382,6 +391,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16(
       dqa[mt] = mfma32(lds_tr8<D>(sk, r0, d0, j16), g0, dqa[mt]);
       dqa[mt] = mfma32(lds_tr8<D>(sk, r0 + 16, d0, j16), g1, dqa[mt]);
     }
+    rows_to_offsets<D>(offs_n, rows_n, tid);
   }
 
   // sum the two kh partials

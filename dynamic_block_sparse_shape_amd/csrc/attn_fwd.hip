@@ -99,8 +99,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
   }
 
 // One KV block t (in buffer t % 2): publish staged block t+1 into the other
-// buffer, refill that stage with block t+3, advance the row / id prefetch,
-// compute block t.
+// buffer, load the rows of block t+4, refill the stage with block t+3,
+// compute block t, then turn the rows into offsets.
 #define PRISM_FWD_STEP(T_, BUF_, KS_, VS_)                                  \
   {                                                                         \
     const int tt = (T_);                                                    \
@@ -108,12 +108,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
     stage_store<D>(KS_, smem + (1 - (BUF_)) * 2 * TL::kBytes, tid);         \
     stage_store<D>(VS_, smem + (1 - (BUF_)) * 2 * TL::kBytes + TL::kBytes,  \
                    tid);                                                    \
+    int rows_n[TL::kPerThread];                                             \
+    stage_rows<D>(rows_n, pb, j_n, tid);                                    \
+    pin_order();                                                            \
     stage_load<D>(KS_, rk, offs_n);                                         \
     stage_load<D>(VS_, rv, offs_n);                                         \
-    stage_offsets<D>(offs_n, pb, j_n, tid);                                 \
+    pin_order();                                                            \
     j_n = lst[min(tt + 5, last)];                                           \
     compute_block(smem + (BUF_) * 2 * TL::kBytes,                           \
                   smem + (BUF_) * 2 * TL::kBytes + TL::kBytes);             \
+    rows_to_offsets<D>(offs_n, rows_n, tid);                                \
   }
 
   auto compute_block = [&](const unsigned char* sk, const unsigned char* sv)

@@ -119,16 +119,42 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(
       0x00020000);
 }
 
-// Byte offsets (within the head) of this thread's pieces of block j.
+// Token rows of this thread's pieces of block j (plain loads of the
+// permutation).  They are issued before a block's tile loads and turned into
+// offsets only after them: wait counters retire loads in issue order, so a
+// row load issued after a tile load would make its first use wait for that
+// tile load too.
+template <int D>
+__device__ __forceinline__ void stage_rows(int* rows,
+                                           const int32_t* __restrict__ pb,
+                                           int j, int tid) {
+#pragma unroll
+  for (int t = 0; t < Tile<D>::kPerThread; ++t)
+    rows[t] = pb[64 * j + Tile<D>::row_of(tid, t)];
+}
+
+// Byte offsets (within the head) of this thread's pieces, from its rows.
+template <int D>
+__device__ __forceinline__ void rows_to_offsets(uint32_t* offs, const int* rows,
+                                                int tid) {
+  const uint32_t p16 = (uint32_t)Tile<D>::piece_of(tid) * 16u;
+#pragma unroll
+  for (int t = 0; t < Tile<D>::kPerThread; ++t)
+    offs[t] = (uint32_t)rows[t] * (uint32_t)(D * 2) + p16;
+}
+
 template <int D>
 __device__ __forceinline__ void stage_offsets(uint32_t* offs,
                                               const int32_t* __restrict__ pb,
                                               int j, int tid) {
-  const uint32_t p16 = (uint32_t)Tile<D>::piece_of(tid) * 16u;
-#pragma unroll
-  for (int t = 0; t < Tile<D>::kPerThread; ++t)
-    offs[t] = (uint32_t)pb[64 * j + Tile<D>::row_of(tid, t)] * (uint32_t)(D * 2) + p16;
+  int rows[Tile<D>::kPerThread];
+  stage_rows<D>(rows, pb, j, tid);
+  rows_to_offsets<D>(offs, rows, tid);
 }
+
+// Keeps the compiler's scheduler from moving instructions across this point
+// (used to pin the issue order of loads).
+__device__ __forceinline__ void pin_order() { __builtin_amdgcn_sched_barrier(0); }
 
 template <int D>
 __device__ __forceinline__ void stage_load(Stage<D>& s, __amdgpu_buffer_rsrc_t r,
