@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
   const int brow = 32 * kh + c;               // K / V row of this lane's column
   {
     // this KV block's K and V stay in LDS for the whole kernel (B operands)
-    uint32_t o0[TL::kPerThread];
+    uint32_t o0[Share<D>::kPerThread];
     Stage<D> ks0, vs0;
     stage_offsets<D>(o0, pb, j, tid);
     stage_load<D>(ks0, head_rsrc<D>(k, head, N), o0);
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
   const float xscale = tid < 64 ? kLog2e : 1.f;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc<D>(q, head, N);
   const __amdgpu_buffer_rsrc_t ro = head_rsrc<D>(d_o, head, N);
-  uint32_t offs_n[TL::kPerThread];
+  uint32_t offs_n[Share<D>::kPerThread];
   int xrow_n = 0;
   int i_n = 0;
   const int last = cnt - 1;
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
     return pb[64 * blk + (tid & 63)];
   };
   if (cnt > 0) {
-    uint32_t o0[TL::kPerThread];
+    uint32_t o0[Share<D>::kPerThread];
     stage_offsets<D>(o0, pb, qlist[0], tid);
     stage_load<D>(qS, rq, o0);
     stage_load<D>(oS, ro, o0);
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
     // small loads first (block t+1's lse / D, block t+2's rows), then the
     // tiles of block t+1: the small ones retire without waiting for those
     const float xS_n = xsrc[xrow_n];
-    int rows_n[TL::kPerThread];
+    int rows_n[Share<D>::kPerThread];
     stage_rows<D>(rows_n, pb, i_n, tid);
     const int xrow_nn = xload(i_n);
     stage_load<D>(qS, rq, offs_n);
@@ -347,11 +347,11 @@ __global__ __launch_bounds__(256, 2) void dq_bf16(
   Stage<D> kS, vS;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(k, head, N);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(v, head, N);
-  uint32_t offs_n[TL::kPerThread];
+  uint32_t offs_n[Share<D>::kPerThread];
   const int last = cnt - 1;
   int j_n;
   {
-    uint32_t o0[TL::kPerThread];
+    uint32_t o0[Share<D>::kPerThread];
     stage_offsets<D>(o0, pb, lst[0], tid);
     stage_load<D>(kS, rk, o0);
     stage_load<D>(vS, rv, o0);
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16(
     stage_store<D>(kS, sk, tid);
     stage_store<D>(vS, sv, tid);
     __syncthreads();
-    int rows_n[TL::kPerThread];
+    int rows_n[Share<D>::kPerThread];
     stage_rows<D>(rows_n, pb, j_n, tid);
     pin_order();
     stage_load<D>(kS, rk, offs_n);

@@ -19,16 +19,20 @@
 namespace prism {
 namespace {
 
-// One workgroup (4 waves) per (b, h, query block).  Wave w = (qh, kh):
-// queries 32*qh .. 32*qh+31 against KV rows 32*kh .. 32*kh+31 of every
-// listed block, so every 32x32 MFMA tile is reused over a 128-deep (S) or
-// 32-deep (P*V) contraction and each K/V byte in LDS is read by two waves.
-// The two kh waves of a query half keep separate online-softmax states and
-// are merged once at the end (exactly as a split over KV).  K and V stay
-// row-major in LDS; V^T fragments come from ds_read_b64_tr_b16.  Blocks are
-// staged two ahead through registers.
+// One workgroup (8 waves) per pair of neighbouring query blocks (2p, 2p+1),
+// which select largely the same KV blocks.  The two lists are merged into
+// one ascending union in LDS; each K/V block of the union is gathered from
+// HBM once and serves both query blocks, so the gather traffic drops to the
+// union's share.  Waves 0-3 own query block 2p and waves 4-7 block 2p+1;
+// within a half, wave (qh, kh) computes queries 32*qh .. +31 against KV rows
+// 32*kh .. +31 of every block, so each 32x32 MFMA tile is reused over a
+// 128-deep (S) or 32-deep (P*V) contraction.  A half skips the union blocks
+// its own list does not hold.  The two kh waves of a query half keep
+// separate online-softmax states, merged once at the end (exactly as a
+// split over KV).  K and V stay row-major in LDS; V^T fragments come from
+// ds_read_b64_tr_b16.  Blocks are staged two ahead through registers.
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
+__global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ kv_idx,
@@ -36,34 +40,92 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
     uint16_t* __restrict__ o, float* __restrict__ lse) {
   using namespace tiles;
   using TL = Tile<D>;
+  using SH = Share<D, 512>;
   constexpr int KS = D / 16;     // k-steps of S^T = K Q^T
   constexpr int DT = D / 32;     // 32-row d tiles of O^T
-  // two LDS buffers (K and V of one block each): block t+1 is published into
-  // one while block t is read from the other -- one barrier per block
-  __shared__ __align__(16) unsigned char smem[4 * TL::kBytes];
-  __shared__ float sm_m[2][32], sm_l[2][32];
-
   const int Nb = N / 64;
+  const int words = (Nb + 31) / 32;
+  // two LDS buffers (K and V of one block each): block t+1 is published into
+  // one while block t is read from the other -- one barrier per block.  Then
+  // the union list (one entry per block: id | in-first << 16 |
+  // in-second << 17) and the two membership bitmaps.
+  extern __shared__ __align__(16) unsigned char dyn[];
+  unsigned char* smem = dyn;
+  uint32_t* ulist = reinterpret_cast<uint32_t*>(dyn + 4 * TL::kBytes);
+  uint32_t* bits = ulist + Nb;
+  __shared__ float sm_m[2][2][32], sm_l[2][2][32];
+  __shared__ int s_cnt[8];
+
   long long bh;
-  int i;
-  if (!xcd_item(Nb, total, bh, i)) return;
+  int pr;
+  if (!xcd_item((Nb + 1) / 2, total, bh, pr)) return;
   const int b = (int)(bh / Hh);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int qh = wave & 1, kh = wave >> 1;
+  const int half = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int qh = wave & 1, kh = (wave >> 1) & 1;
   const int c = lane & 31, hf = lane >> 5, j16 = lane & 15, grp = lane >> 4;
   const long long head = bh * N;
   const int32_t* pb = perm + (long long)b * N;
+  const int i0 = 2 * pr;
+  const bool has_second = i0 + 1 < Nb;   // odd Nb: the last pair is a single
+  const long long row0 = bh * Nb + i0;
+  const int cnt0 = counts[row0];
+  const int cnt1 = has_second ? counts[row0 + 1] : 0;
+  const int32_t* lst0 = kv_idx + row0 * (long long)capacity;
+  const int32_t* lst1 = lst0 + capacity;
 
-  const int qrow = pb[64 * i + 32 * qh + c];
+  // ---- ascending union of the two lists
+  for (int w = tid; w < 2 * words; w += 512) bits[w] = 0u;
+  __syncthreads();
+  for (int t = tid; t < cnt0; t += 512) {
+    const int j = lst0[t];
+    atomicOr(&bits[j >> 5], 1u << (j & 31));
+  }
+  for (int t = tid; t < cnt1; t += 512) {
+    const int j = lst1[t];
+    atomicOr(&bits[words + (j >> 5)], 1u << (j & 31));
+  }
+  __syncthreads();
+  int ucnt = 0;
+  {
+    // thread w owns bitmap word w (Nb <= 8192 = 32 * 256)
+    const uint32_t wa = tid < words ? bits[tid] : 0u;
+    const uint32_t wb = tid < words ? bits[words + tid] : 0u;
+    uint32_t wu = wa | wb;
+    const int n = __popc(wu);
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int x = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += x;
+    }
+    if (lane == 63) s_cnt[wave] = incl;
+    __syncthreads();
+    int pos = incl - n;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int x = s_cnt[w];
+      pos += w < wave ? x : 0;
+      ucnt += x;
+    }
+    while (wu) {
+      const int bit = __ffs(wu) - 1;
+      ulist[pos++] = (uint32_t)(tid * 32 + bit) | (((wa >> bit) & 1u) << 16) |
+                     (((wb >> bit) & 1u) << 17);
+      wu &= wu - 1u;
+    }
+  }
+  __syncthreads();
+
+  // a missing second block borrows the first one's rows (never written)
+  const int iq = (half == 1 && has_second) ? i0 + 1 : i0;
+  const int qrow = pb[64 * iq + 32 * qh + c];
   bf16x8 qreg[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     qreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(
         q + (head + qrow) * D + 16 * ks + 8 * hf));
-
-  const long long rowid = bh * Nb + i;
-  const int cnt = counts[rowid];
-  const int32_t* lst = kv_idx + rowid * (long long)capacity;
+  const uint32_t mflag = 1u << (16 + half);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 oacc[DT];
@@ -71,53 +133,59 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
   for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
   const int krow = 32 * kh + slot_of(c);   // K row feeding this lane's M-row
 
-  Stage<D> kA, vA, kB, vB;
+  Stage<D, 512> kA, vA, kB, vB;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(k, head, N);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(v, head, N);
-  uint32_t offs_n[TL::kPerThread];
+  uint32_t offs_n[SH::kPerThread];
+  const int last = ucnt - 1;
+  auto uid = [&](int t) __attribute__((always_inline)) -> int {
+    return (int)(ulist[min(t, last)] & 0xffffu);
+  };
   int j_n = 0;
   // prologue: block 0 published to buffer 0, block 1 staged, block 2 in
   // flight, offsets of block 3, id of block 4.  Past the end of the list the
-  // last block is re-fetched, so the loop body has no branches and the
-  // compiler's wait counters stay exact.
-  const int last = cnt - 1;
+  // last block is re-fetched, so the loop body has no branches around the
+  // loads and the compiler's wait counters stay exact.
   {
-    uint32_t o0[TL::kPerThread];
-    stage_offsets<D>(o0, pb, lst[0], tid);
-    stage_load<D>(kA, rk, o0);
-    stage_load<D>(vA, rv, o0);
-    stage_offsets<D>(o0, pb, lst[min(1, last)], tid);
-    stage_load<D>(kB, rk, o0);
-    stage_load<D>(vB, rv, o0);
-    stage_store<D>(kA, smem, tid);
-    stage_store<D>(vA, smem + TL::kBytes, tid);
-    stage_offsets<D>(o0, pb, lst[min(2, last)], tid);
-    stage_load<D>(kA, rk, o0);
-    stage_load<D>(vA, rv, o0);
-    stage_offsets<D>(offs_n, pb, lst[min(3, last)], tid);
-    j_n = lst[min(4, last)];
+    uint32_t o0[SH::kPerThread];
+    stage_offsets<D, 512>(o0, pb, uid(0), tid);
+    stage_load<D, 512>(kA, rk, o0);
+    stage_load<D, 512>(vA, rv, o0);
+    stage_offsets<D, 512>(o0, pb, uid(1), tid);
+    stage_load<D, 512>(kB, rk, o0);
+    stage_load<D, 512>(vB, rv, o0);
+    stage_store<D, 512>(kA, smem, tid);
+    stage_store<D, 512>(vA, smem + TL::kBytes, tid);
+    stage_offsets<D, 512>(o0, pb, uid(2), tid);
+    stage_load<D, 512>(kA, rk, o0);
+    stage_load<D, 512>(vA, rv, o0);
+    stage_offsets<D, 512>(offs_n, pb, uid(3), tid);
+    j_n = uid(4);
   }
 
-// One KV block t (in buffer t % 2): publish staged block t+1 into the other
-// buffer, load the rows of block t+4, refill the stage with block t+3,
-// compute block t, then turn the rows into offsets.
+// One union block t (in buffer t % 2): publish staged block t+1 into the
+// other buffer, load the rows of block t+4, refill the stage with block t+3,
+// compute block t if this half's list holds it, then turn the rows into
+// offsets.
 #define PRISM_FWD_STEP(T_, BUF_, KS_, VS_)                                  \
   {                                                                         \
     const int tt = (T_);                                                    \
     __syncthreads();                                                        \
-    stage_store<D>(KS_, smem + (1 - (BUF_)) * 2 * TL::kBytes, tid);         \
-    stage_store<D>(VS_, smem + (1 - (BUF_)) * 2 * TL::kBytes + TL::kBytes,  \
-                   tid);                                                    \
-    int rows_n[TL::kPerThread];                                             \
-    stage_rows<D>(rows_n, pb, j_n, tid);                                    \
+    stage_store<D, 512>(KS_, smem + (1 - (BUF_)) * 2 * TL::kBytes, tid);    \
+    stage_store<D, 512>(VS_, smem + (1 - (BUF_)) * 2 * TL::kBytes +         \
+                                 TL::kBytes, tid);                          \
+    int rows_n[SH::kPerThread];                                             \
+    stage_rows<D, 512>(rows_n, pb, j_n, tid);                               \
     pin_order();                                                            \
-    stage_load<D>(KS_, rk, offs_n);                                         \
-    stage_load<D>(VS_, rv, offs_n);                                         \
+    stage_load<D, 512>(KS_, rk, offs_n);                                    \
+    stage_load<D, 512>(VS_, rv, offs_n);                                    \
     pin_order();                                                            \
-    j_n = lst[min(tt + 5, last)];                                           \
-    compute_block(smem + (BUF_) * 2 * TL::kBytes,                           \
-                  smem + (BUF_) * 2 * TL::kBytes + TL::kBytes);             \
-    rows_to_offsets<D>(offs_n, rows_n, tid);                                \
+    j_n = uid(tt + 5);                                                      \
+    const uint32_t e = __builtin_amdgcn_readfirstlane(ulist[tt]);           \
+    if (e & mflag)                                                          \
+      compute_block(smem + (BUF_) * 2 * TL::kBytes,                         \
+                    smem + (BUF_) * 2 * TL::kBytes + TL::kBytes);           \
+    rows_to_offsets<D, 512>(offs_n, rows_n, tid);                           \
   }
 
   auto compute_block = [&](const unsigned char* sk, const unsigned char* sv)
@@ -164,21 +232,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
 
   // stage B holds block t+1 at even t, stage A at odd t
   int t = 0;
-  for (; t + 1 < cnt; t += 2) {
+  for (; t + 1 < ucnt; t += 2) {
     PRISM_FWD_STEP(t, 0, kB, vB)
     PRISM_FWD_STEP(t + 1, 1, kA, vA)
   }
-  if (t < cnt) PRISM_FWD_STEP(t, 0, kB, vB)
+  if (t < ucnt) PRISM_FWD_STEP(t, 0, kB, vB)
 #undef PRISM_FWD_STEP
 
-  // merge the two KV halves: waves kh = 1 hand over (m, l, O) through LDS
+  // merge the two KV halves of each query half: waves kh = 1 hand over
+  // (m, l, O) through LDS (2 waves x 64 lanes x D/2 floats = 2 * kBytes per
+  // query block)
   __syncthreads();
-  // 2 waves x 64 lanes x (D/2) floats = 2 * TL::kBytes
-  float* xo = reinterpret_cast<float*>(smem);
+  float* xo = reinterpret_cast<float*>(smem + half * 2 * TL::kBytes);
   if (kh == 1) {
     if (hf == 0) {
-      sm_m[qh][c] = m_run;
-      sm_l[qh][c] = l_run;
+      sm_m[half][qh][c] = m_run;
+      sm_l[half][qh][c] = l_run;
     }
 #pragma unroll
     for (int mt = 0; mt < DT; ++mt)
@@ -187,8 +256,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
         xo[((qh * 64 + lane) * DT + mt) * 16 + r] = oacc[mt][r];
   }
   __syncthreads();
-  if (kh == 0) {
-    const float m2 = sm_m[qh][c], l2 = sm_l[qh][c];
+  if (kh == 0 && (half == 0 || has_second)) {
+    const float m2 = sm_m[half][qh][c], l2 = sm_l[half][qh][c];
     const float m = fmaxf(m_run, m2);
     const float a1 = exp2_fast(m_run - m), a2 = exp2_fast(m2 - m);
     const float l = l_run * a1 + l2 * a2;
@@ -272,17 +341,22 @@ prism_status launch_attn_fwd(const void* q, const void* k, const void* v,
   if (dtype == PRISM_BF16) {
     const float sl2 = scale * tiles::kLog2e;
     const long long total = (long long)B * Hh;   // (batch, head) pairs
-    const dim3 g1(tiles::xcd_grid(N / 64, total));
-    if (d == 128)
-      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<128>, g1, dim3(256), 0, stream,
+    const int Nb = N / 64;
+    const dim3 g1(tiles::xcd_grid((Nb + 1) / 2, total));
+    const size_t words = (size_t)(Nb + 31) / 32;
+    if (d == 128) {
+      const size_t dyn = 4 * tiles::Tile<128>::kBytes + 4 * (size_t)Nb + 8 * words;
+      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<128>, g1, dim3(512), dyn, stream,
                    (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                    perm, counts, kv_idx, capacity, Hh, N, total, sl2,
                    (uint16_t*)o, lse);
-    else
-      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<64>, g1, dim3(256), 0, stream,
+    } else {
+      const size_t dyn = 4 * tiles::Tile<64>::kBytes + 4 * (size_t)Nb + 8 * words;
+      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<64>, g1, dim3(512), dyn, stream,
                    (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                    perm, counts, kv_idx, capacity, Hh, N, total, sl2,
                    (uint16_t*)o, lse);
+    }
   } else {
     if (d == 128)
       PRISM_LAUNCH("attn_fwd_f32", attn_fwd_f32<128>, grid, dim3(64), 0, stream,

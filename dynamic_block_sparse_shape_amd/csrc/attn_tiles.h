@@ -55,7 +55,6 @@ struct Tile {
   static constexpr int kRowBytes = D * 2;
   static constexpr int kPieces = kRowBytes / 16;          // 16-byte pieces per row
   static constexpr int kBytes = 64 * kRowBytes;
-  static constexpr int kPerThread = 64 * kPieces / 256;   // pieces per thread
 
   __device__ static __forceinline__ int swz(int r) {
     if constexpr (kPieces == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
@@ -69,12 +68,19 @@ struct Tile {
   __device__ static __forceinline__ int off8(int r, int d) {
     return off(r, d >> 3) + ((d & 4) << 1);
   }
-  // row of piece slot t of this thread
+};
+
+// How NT threads share the 16-byte pieces of one tile: thread tid owns
+// piece tid % kPieces of rows (tid + NT * t) / kPieces, t < kPerThread.
+template <int D, int NT = 256>
+struct Share {
+  static constexpr int kPerThread = 64 * Tile<D>::kPieces / NT;
+  static_assert(kPerThread >= 1, "too many threads for one tile");
   __device__ static __forceinline__ int row_of(int tid, int t) {
-    return (tid + 256 * t) / kPieces;
+    return (tid + NT * t) / Tile<D>::kPieces;
   }
   __device__ static __forceinline__ int piece_of(int tid) {
-    return tid % kPieces;
+    return tid % Tile<D>::kPieces;
   }
 };
 
@@ -104,9 +110,9 @@ __device__ __forceinline__ bf16x8 lds_tr8(const unsigned char* tile, int r0,
 // Global -> register staging of one 64-row tile.  Rows are gathered with
 // buffer loads: one resource per (tensor, head) and 32-bit byte offsets that
 // the K and V (or Q and dO) tiles of a block share.
-template <int D>
+template <int D, int NT = 256>
 struct Stage {
-  u32x4 v[Tile<D>::kPerThread];   // clang vectors: promotable to registers
+  u32x4 v[Share<D, NT>::kPerThread];   // clang vectors: promotable to registers
 };
 
 // Buffer resource over one head's [N, D] bf16 rows (loads past the end
@@ -124,53 +130,53 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(
 // offsets only after them: wait counters retire loads in issue order, so a
 // row load issued after a tile load would make its first use wait for that
 // tile load too.
-template <int D>
+template <int D, int NT = 256>
 __device__ __forceinline__ void stage_rows(int* rows,
                                            const int32_t* __restrict__ pb,
                                            int j, int tid) {
 #pragma unroll
-  for (int t = 0; t < Tile<D>::kPerThread; ++t)
-    rows[t] = pb[64 * j + Tile<D>::row_of(tid, t)];
+  for (int t = 0; t < Share<D, NT>::kPerThread; ++t)
+    rows[t] = pb[64 * j + Share<D, NT>::row_of(tid, t)];
 }
 
 // Byte offsets (within the head) of this thread's pieces, from its rows.
-template <int D>
+template <int D, int NT = 256>
 __device__ __forceinline__ void rows_to_offsets(uint32_t* offs, const int* rows,
                                                 int tid) {
-  const uint32_t p16 = (uint32_t)Tile<D>::piece_of(tid) * 16u;
+  const uint32_t p16 = (uint32_t)Share<D, NT>::piece_of(tid) * 16u;
 #pragma unroll
-  for (int t = 0; t < Tile<D>::kPerThread; ++t)
+  for (int t = 0; t < Share<D, NT>::kPerThread; ++t)
     offs[t] = (uint32_t)rows[t] * (uint32_t)(D * 2) + p16;
 }
 
-template <int D>
+template <int D, int NT = 256>
 __device__ __forceinline__ void stage_offsets(uint32_t* offs,
                                               const int32_t* __restrict__ pb,
                                               int j, int tid) {
-  int rows[Tile<D>::kPerThread];
-  stage_rows<D>(rows, pb, j, tid);
-  rows_to_offsets<D>(offs, rows, tid);
+  int rows[Share<D, NT>::kPerThread];
+  stage_rows<D, NT>(rows, pb, j, tid);
+  rows_to_offsets<D, NT>(offs, rows, tid);
 }
 
 // Keeps the compiler's scheduler from moving instructions across this point
 // (used to pin the issue order of loads).
 __device__ __forceinline__ void pin_order() { __builtin_amdgcn_sched_barrier(0); }
 
-template <int D>
-__device__ __forceinline__ void stage_load(Stage<D>& s, __amdgpu_buffer_rsrc_t r,
+template <int D, int NT = 256>
+__device__ __forceinline__ void stage_load(Stage<D, NT>& s, __amdgpu_buffer_rsrc_t r,
                                            const uint32_t* offs) {
 #pragma unroll
-  for (int t = 0; t < Tile<D>::kPerThread; ++t)
+  for (int t = 0; t < Share<D, NT>::kPerThread; ++t)
     s.v[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, offs[t], 0, 0));
 }
 
-template <int D>
-__device__ __forceinline__ void stage_store(const Stage<D>& s,
+template <int D, int NT = 256>
+__device__ __forceinline__ void stage_store(const Stage<D, NT>& s,
                                             unsigned char* tile, int tid) {
-  const int p = Tile<D>::piece_of(tid);
+  const int p = Share<D, NT>::piece_of(tid);
 #pragma unroll
-  for (int t = 0; t < Tile<D>::kPerThread; ++t)
-    *reinterpret_cast<u32x4*>(tile + Tile<D>::off(Tile<D>::row_of(tid, t), p)) =
+  for (int t = 0; t < Share<D, NT>::kPerThread; ++t)
+    *reinterpret_cast<u32x4*>(tile + Tile<D>::off(Share<D, NT>::row_of(tid, t), p)) =
         s.v[t];
 }
 
