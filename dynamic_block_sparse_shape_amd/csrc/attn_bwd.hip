@@ -82,15 +82,20 @@ __global__ void bitmap_build(const int32_t* __restrict__ counts,
 }
 
 // ------------------------------------------------------- dK / dV (bf16)
-// One workgroup per KV block, 4 waves = (kh, qh): KV rows 32*kh .. +31 (K, V
-// tiles resident in LDS, B operands) against query rows 32*qh .. +31 of
-// every query block that selected this KV block.  The column bitmap is
-// compacted into an ascending list in LDS first; Q and dO tiles (plus lse,
-// D) are staged one block ahead through registers into swizzled LDS
-// tiles.  Q^T / dO^T fragments come from ds_read_b64_tr_b16.  The two qh
-// waves of a KV half sum their partial dK / dV at the end.
+// One workgroup (8 waves) per pair of neighbouring KV blocks (2p, 2p+1),
+// which are selected by largely the same query blocks.  The two column
+// bitmaps are merged into one ascending union of query blocks (entries
+// id | (selects 2p) << 13 | (selects 2p+1) << 14, 16 bits each) and each
+// query block's Q, dO, lse and D are gathered once for both.  Waves 0-3 own
+// KV block 2p and waves 4-7 block 2p+1; within a half, wave (kh, qh)
+// computes KV rows 32*kh .. +31 (K, V of the block resident in LDS, B
+// operands) against query rows 32*qh .. +31.  A half skips the query blocks
+// that did not select its KV block.  Q and dO go through two LDS buffers,
+// staged one block ahead in registers; Q^T / dO^T fragments come from
+// ds_read_b64_tr_b16.  The two qh waves of a KV half sum their partial dK /
+// dV at the end.
 template <int D>
-__global__ __launch_bounds__(256, 2) void dkdv_bf16(
+__global__ __launch_bounds__(512, 2) void dkdv_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta,
@@ -99,71 +104,97 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
     float* __restrict__ dk, float* __restrict__ dv) {
   using namespace tiles;
   using TL = Tile<D>;
+  using SH = Share<D, 512>;
   constexpr int KS = D / 16, DT = D / 32;
   extern __shared__ __align__(16) unsigned char dyn[];
-  unsigned char* sq = dyn;                              // Q tile
-  unsigned char* sdo = dyn + TL::kBytes;                // dO tile
-  unsigned char* skt = dyn + 2 * TL::kBytes;            // this block's K
-  unsigned char* svt = dyn + 3 * TL::kBytes;            // this block's V
-  float* s_lse = reinterpret_cast<float*>(dyn + 4 * TL::kBytes);   // [64]
-  float* s_dlt = s_lse + 64;                                       // [64]
-  int* s_cnt = reinterpret_cast<int*>(s_dlt + 64);                 // [8]
-  uint16_t* qlist = reinterpret_cast<uint16_t*>(s_cnt + 8);        // [Nb]
+  unsigned char* sqo = dyn;                         // buffer u: Q, dO tiles
+  unsigned char* skv = dyn + 4 * TL::kBytes;        // half h: K, V tiles
+  float* sx = reinterpret_cast<float*>(dyn + 8 * TL::kBytes);  // buffer u: lse, D
+  uint16_t* ulist = reinterpret_cast<uint16_t*>(sx + 256);
+  __shared__ int s_cnt[8];
 
   const int Nb = N / 64;
   long long bh;
-  int j;
-  if (!xcd_item(Nb, heads, bh, j)) return;
+  int pr;
+  if (!xcd_item((Nb + 1) / 2, heads, bh, pr)) return;
   const int b = (int)(bh / Hh);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int kh = wave & 1, qh = wave >> 1;
+  const int half = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int kh = wave & 1, qh = (wave >> 1) & 1;
   const int c = lane & 31, hf = lane >> 5, j16 = lane & 15, grp = lane >> 4;
   const long long head = bh * N;
   const int32_t* pb = perm + (long long)b * N;
   const float sl2 = scale * kLog2e;
+  const int j0 = 2 * pr;
+  const bool has_second = j0 + 1 < Nb;
+  const int j1 = has_second ? j0 + 1 : j0;
 
-  // ascending list of the query blocks that selected block j: popcount
-  // prefix over the column's words, then each thread writes its set bits
-  const uint32_t* col = bits + (bh * Nb + j) * words;
-  if (tid == 0) s_cnt[0] = 0;
-  __syncthreads();
-  for (int w0 = 0; w0 < words; w0 += 256) {
-    const int w = w0 + tid;
-    const uint32_t word = w < words ? col[w] : 0u;
-    const int n = __popc(word);
+  // ---- ascending union of the two columns (thread w owns word w)
+  int ucnt = 0;
+  {
+    const uint32_t* col0 = bits + (bh * Nb + j0) * words;
+    const uint32_t wa = tid < words ? col0[tid] : 0u;
+    const uint32_t wb = (tid < words && has_second) ? col0[words + tid] : 0u;
+    uint32_t wu = wa | wb;
+    const int n = __popc(wu);
     int incl = n;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
+      const int x = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += x;
     }
-    if (lane == 63) s_cnt[1 + wave] = incl;
+    if (lane == 63) s_cnt[wave] = incl;
     __syncthreads();
-    int pos = s_cnt[0] + incl - n;
-    for (int x = 0; x < wave; ++x) pos += s_cnt[1 + x];
-    uint32_t wd = word;
-    while (wd) {
-      qlist[pos++] = (uint16_t)(w * 32 + __ffs(wd) - 1);
-      wd &= wd - 1;
+    int pos = incl - n;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int x = s_cnt[w];
+      pos += w < wave ? x : 0;
+      ucnt += x;
     }
-    __syncthreads();
-    if (tid == 0) s_cnt[0] += (s_cnt[1] + s_cnt[2]) + (s_cnt[3] + s_cnt[4]);
-    __syncthreads();
+    while (wu) {
+      const int bit = __ffs(wu) - 1;
+      ulist[pos++] = (uint16_t)((tid * 32 + bit) | (((wa >> bit) & 1u) << 13) |
+                                (((wb >> bit) & 1u) << 14));
+      wu &= wu - 1u;
+    }
   }
-  const int cnt = s_cnt[0];
-
-  const int kvrow = pb[64 * j + 32 * kh + c];
-  const int brow = 32 * kh + c;               // K / V row of this lane's column
   {
-    // this KV block's K and V stay in LDS for the whole kernel (B operands)
-    uint32_t o0[Share<D>::kPerThread];
-    Stage<D> ks0, vs0;
-    stage_offsets<D>(o0, pb, j, tid);
-    stage_load<D>(ks0, head_rsrc<D>(k, head, N), o0);
-    stage_load<D>(vs0, head_rsrc<D>(v, head, N), o0);
-    stage_store<D>(ks0, skt, tid);
-    stage_store<D>(vs0, svt, tid);
+    // K and V of both KV blocks stay in LDS for the whole kernel
+    uint32_t o0[SH::kPerThread];
+    Stage<D, 512> ks0, vs0;
+    const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(k, head, N);
+    const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(v, head, N);
+    stage_offsets<D, 512>(o0, pb, j0, tid);
+    stage_load<D, 512>(ks0, rk, o0);
+    stage_load<D, 512>(vs0, rv, o0);
+    stage_store<D, 512>(ks0, skv, tid);
+    stage_store<D, 512>(vs0, skv + TL::kBytes, tid);
+    stage_offsets<D, 512>(o0, pb, j1, tid);
+    stage_load<D, 512>(ks0, rk, o0);
+    stage_load<D, 512>(vs0, rv, o0);
+    stage_store<D, 512>(ks0, skv + 2 * TL::kBytes, tid);
+    stage_store<D, 512>(vs0, skv + 3 * TL::kBytes, tid);
   }
+  __syncthreads();
+  if (ucnt == 0) {
+    // no query block selected either KV block: zero gradients
+    if (qh == 0 && (half == 0 || has_second)) {
+      const int kvr = pb[64 * (half ? j1 : j0) + 32 * kh + c];
+      float4* dvr = reinterpret_cast<float4*>(dv + (head + kvr) * D);
+      float4* dkr = reinterpret_cast<float4*>(dk + (head + kvr) * D);
+      for (int e = hf; e < D / 4; e += 2) {
+        dvr[e] = float4{0.f, 0.f, 0.f, 0.f};
+        dkr[e] = float4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    return;
+  }
+
+  const int kvrow = pb[64 * (half ? j1 : j0) + 32 * kh + c];
+  const int brow = 32 * kh + c;               // K / V row of this lane's column
+  const unsigned char* skt = skv + half * 2 * TL::kBytes;
+  const unsigned char* svt = skt + TL::kBytes;
   f32x16 dva[DT], dka[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) {
@@ -173,51 +204,54 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
   // C-layout register 4a + b of this lane holds query row
   // qbase(a) + b, qbase(a) = 32 qh + 16 (a / 2) + 8 hf + 4 (a % 2)
   const int arow = 32 * qh + slot_of(c);      // Q / dO row of this lane's M-row
+  const uint32_t mflag = 1u << (13 + half);
 
-  // one query block staged ahead in registers; past the end of the list the
-  // last block is re-fetched (branch-free loop body)
-  Stage<D> qS, oS;
-  // lse (tid < 64) or D (64 <= tid < 128) of one row of the staged block;
-  // scaled to log2 units when it is published
-  float xS = 0.f;
+  // Q / dO tiles and one lse (tid < 64) or D (64 <= tid < 128) per thread
+  // are staged one block ahead in registers and published into two LDS
+  // buffers; lse is scaled to log2 units when it is published
   const float* xsrc = (tid < 64 ? lse : delta) + head;
   const float xscale = tid < 64 ? kLog2e : 1.f;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc<D>(q, head, N);
   const __amdgpu_buffer_rsrc_t ro = head_rsrc<D>(d_o, head, N);
-  uint32_t offs_n[Share<D>::kPerThread];
+  Stage<D, 512> qS, oS;
+  float xS = 0.f;
+  uint32_t offs_n[SH::kPerThread];
   int xrow_n = 0;
-  int i_n = 0;
-  const int last = cnt - 1;
+  const int last = ucnt - 1;
+  auto uid = [&](int t) __attribute__((always_inline)) -> int {
+    return (int)(ulist[min(t, last)] & 0x1fffu);
+  };
   auto xload = [&](int blk) __attribute__((always_inline)) -> int {
     return pb[64 * blk + (tid & 63)];
   };
-  if (cnt > 0) {
-    uint32_t o0[Share<D>::kPerThread];
-    stage_offsets<D>(o0, pb, qlist[0], tid);
-    stage_load<D>(qS, rq, o0);
-    stage_load<D>(oS, ro, o0);
-    xS = xsrc[xload(qlist[0])];
-    stage_offsets<D>(offs_n, pb, qlist[min(1, last)], tid);
-    xrow_n = xload(qlist[min(1, last)]);
-    i_n = qlist[min(2, last)];
+  int j_n = 0;
+  {
+    // entry 0 published to buffer 0, entry 1 staged, offsets and lse / D
+    // row of entry 2, id of entry 3
+    uint32_t o0[SH::kPerThread];
+    int u = uid(0);
+    stage_offsets<D, 512>(o0, pb, u, tid);
+    stage_load<D, 512>(qS, rq, o0);
+    stage_load<D, 512>(oS, ro, o0);
+    xS = xsrc[xload(u)];
+    stage_store<D, 512>(qS, sqo, tid);
+    stage_store<D, 512>(oS, sqo + TL::kBytes, tid);
+    if (tid < 128) sx[tid] = xS * xscale;
+    u = uid(1);
+    stage_offsets<D, 512>(o0, pb, u, tid);
+    stage_load<D, 512>(qS, rq, o0);
+    stage_load<D, 512>(oS, ro, o0);
+    xS = xsrc[xload(u)];
+    u = uid(2);
+    stage_offsets<D, 512>(offs_n, pb, u, tid);
+    xrow_n = xload(u);
+    j_n = uid(3);
   }
 
-  for (int t = 0; t < cnt; ++t) {
-    __syncthreads();
-    stage_store<D>(qS, sq, tid);
-    stage_store<D>(oS, sdo, tid);
-    if (tid < 128) s_lse[tid] = xS * xscale;     // s_dlt follows s_lse
-    __syncthreads();
-    // small loads first (block t+1's lse / D, block t+2's rows), then the
-    // tiles of block t+1: the small ones retire without waiting for those
-    const float xS_n = xsrc[xrow_n];
-    int rows_n[Share<D>::kPerThread];
-    stage_rows<D>(rows_n, pb, i_n, tid);
-    const int xrow_nn = xload(i_n);
-    stage_load<D>(qS, rq, offs_n);
-    stage_load<D>(oS, ro, offs_n);
-    i_n = qlist[min(t + 3, last)];
-
+  auto compute_block = [&](const unsigned char* sq, const float* s_lse)
+                           __attribute__((always_inline)) {
+    const unsigned char* sdo = sq + TL::kBytes;
+    const float* s_dlt = s_lse + 64;
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -252,16 +286,51 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
       dka[mt] = mfma32(lds_tr8<D>(sq, r0, d0, j16), g0, dka[mt]);
       dka[mt] = mfma32(lds_tr8<D>(sq, r0 + 16, d0, j16), g1, dka[mt]);
     }
-    xS = xS_n;
-    xrow_n = xrow_nn;
-    rows_to_offsets<D>(offs_n, rows_n, tid);
+  };
+
+// One union entry t (in buffer t % 2): publish the staged entry t+1 into the
+// other buffer, load the rows and lse / D of later entries, refill the stage
+// with entry t+2, compute entry t if it selected this half's KV block.
+#define PRISM_DKDV_STEP(T_, BUF_)                                           \
+  {                                                                         \
+    const int tt = (T_);                                                    \
+    __syncthreads();                                                        \
+    stage_store<D, 512>(qS, sqo + (1 - (BUF_)) * 2 * TL::kBytes, tid);      \
+    stage_store<D, 512>(oS, sqo + (1 - (BUF_)) * 2 * TL::kBytes +           \
+                                TL::kBytes, tid);                           \
+    if (tid < 128) sx[(1 - (BUF_)) * 128 + tid] = xS * xscale;              \
+    const float x_n = xsrc[xrow_n];                                         \
+    int rows_n[SH::kPerThread];                                             \
+    stage_rows<D, 512>(rows_n, pb, j_n, tid);                               \
+    const int xrow_nn = xload(j_n);                                         \
+    pin_order();                                                            \
+    stage_load<D, 512>(qS, rq, offs_n);                                     \
+    stage_load<D, 512>(oS, ro, offs_n);                                     \
+    pin_order();                                                            \
+    xS = x_n;                                                               \
+    j_n = uid(tt + 4);                                                      \
+    const uint32_t e = __builtin_amdgcn_readfirstlane((uint32_t)ulist[tt]); \
+    if (e & mflag)                                                          \
+      compute_block(sqo + (BUF_) * 2 * TL::kBytes, sx + (BUF_) * 128);      \
+    rows_to_offsets<D, 512>(offs_n, rows_n, tid);                           \
+    xrow_n = xrow_nn;                                                       \
   }
 
-  // sum the two qh partials: qh = 1 hands over through LDS, one tensor at a
-  // time (2 waves x 64 lanes x D/2 floats = 2 * TL::kBytes)
-  float* xch = reinterpret_cast<float*>(dyn);
+  int t = 0;
+  for (; t + 1 < ucnt; t += 2) {
+    PRISM_DKDV_STEP(t, 0)
+    PRISM_DKDV_STEP(t + 1, 1)
+  }
+  if (t < ucnt) PRISM_DKDV_STEP(t, 0)
+#undef PRISM_DKDV_STEP
+
+  // sum the two qh partials of each KV half: qh = 1 hands over through LDS,
+  // one tensor at a time (2 waves x 64 lanes x D/2 floats = 2 * kBytes per
+  // half)
+  float* xch = reinterpret_cast<float*>(sqo + half * 2 * TL::kBytes);
   float* dvr = dv + (head + kvrow) * D;
   float* dkr = dk + (head + kvrow) * D;
+  const bool write = half == 0 || has_second;
   for (int pass = 0; pass < 2; ++pass) {
     f32x16* acc = pass == 0 ? dva : dka;
     __syncthreads();
@@ -273,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
           xch[((kh * 64 + lane) * DT + mt) * 16 + r] = acc[mt][r];
     }
     __syncthreads();
-    if (qh == 0) {
+    if (qh == 0 && write) {
       float* out = pass == 0 ? dvr : dkr;
       const float f = pass == 0 ? 1.f : scale;
 #pragma unroll
@@ -293,11 +362,14 @@ __global__ __launch_bounds__(256, 2) void dkdv_bf16(
 }
 
 // ------------------------------------------------------------ dQ (bf16)
-// One workgroup per query block, waves (qh, kh) as in the forward: S^T and
-// dP^T per 32x32 tile, dQ^T += K^T dS^T with K^T fragments from
-// ds_read_b64_tr_b16; K and V staged one block ahead.
+// One workgroup (8 waves) per pair of neighbouring query blocks, as in the
+// forward: the union of the two lists is gathered once, waves 0-3 own query
+// block 2p and waves 4-7 block 2p+1, wave (qh, kh) of a half computes S^T
+// and dP^T per 32x32 tile and dQ^T += K^T dS^T with K^T fragments from
+// ds_read_b64_tr_b16.  K and V go through two LDS buffers, staged two
+// blocks ahead in registers.
 template <int D>
-__global__ __launch_bounds__(256, 2) void dq_bf16(
+__global__ __launch_bounds__(512, 2) void dq_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta,
@@ -306,24 +378,37 @@ __global__ __launch_bounds__(256, 2) void dq_bf16(
     long long heads, float scale, float* __restrict__ dq) {
   using namespace tiles;
   using TL = Tile<D>;
+  using SH = Share<D, 512>;
   constexpr int KS = D / 16, DT = D / 32;
-  __shared__ __align__(16) unsigned char smem[2 * TL::kBytes];
-  unsigned char* sk = smem;
-  unsigned char* sv = smem + TL::kBytes;
-
   const int Nb = N / 64;
+  extern __shared__ __align__(16) unsigned char dyn[];
+  unsigned char* smem = dyn;                    // two (K, V) buffers
+  uint32_t* ulist = reinterpret_cast<uint32_t*>(dyn + 4 * TL::kBytes);
+  uint32_t* bits = ulist + Nb;
+  __shared__ int s_cnt[8];
+
   long long bh;
-  int i;
-  if (!xcd_item(Nb, heads, bh, i)) return;
+  int pr;
+  if (!xcd_item((Nb + 1) / 2, heads, bh, pr)) return;
   const int b = (int)(bh / Hh);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int qh = wave & 1, kh = wave >> 1;
+  const int half = __builtin_amdgcn_readfirstlane(wave >> 2);
+  const int qh = wave & 1, kh = (wave >> 1) & 1;
   const int c = lane & 31, hf = lane >> 5, j16 = lane & 15, grp = lane >> 4;
   const long long head = bh * N;
   const int32_t* pb = perm + (long long)b * N;
   const float sl2 = scale * kLog2e;
+  const int i0 = 2 * pr;
+  const bool has_second = i0 + 1 < Nb;
+  const long long row0 = bh * Nb + i0;
+  const int cnt0 = counts[row0];
+  const int cnt1 = has_second ? counts[row0 + 1] : 0;
+  const int32_t* lst0 = kv_idx + row0 * (long long)capacity;
+  const int ucnt = pair_union(lst0, cnt0, lst0 + capacity, cnt1, Nb, bits,
+                              ulist, s_cnt, tid);
 
-  const int qrow = pb[64 * i + 32 * qh + c];
+  const int iq = (half == 1 && has_second) ? i0 + 1 : i0;
+  const int qrow = pb[64 * iq + 32 * qh + c];
   bf16x8 qreg[KS], doreg[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -332,46 +417,40 @@ __global__ __launch_bounds__(256, 2) void dq_bf16(
   }
   const float lse2 = lse[head + qrow] * kLog2e;
   const float dlt = delta[head + qrow];
+  const uint32_t mflag = 1u << (16 + half);
   f32x16 dqa[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dqa[t] = f32x16{};
   const int arow = 32 * kh + slot_of(c);
 
-  const long long rowid = bh * Nb + i;
-  const int cnt = counts[rowid];
-  const int32_t* lst = kv_idx + rowid * (long long)capacity;
-
-  // one block staged ahead in registers (keeps the kernel at 2 waves/SIMD);
-  // past the end of the list the last block is re-fetched, keeping the loop
-  // body free of branches (exact wait counters)
-  Stage<D> kS, vS;
+  Stage<D, 512> kA, vA, kB, vB;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(k, head, N);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(v, head, N);
-  uint32_t offs_n[Share<D>::kPerThread];
-  const int last = cnt - 1;
-  int j_n;
+  uint32_t offs_n[SH::kPerThread];
+  const int last = ucnt - 1;
+  auto uid = [&](int t) __attribute__((always_inline)) -> int {
+    return (int)(ulist[min(t, last)] & 0xffffu);
+  };
+  int j_n = 0;
   {
-    uint32_t o0[Share<D>::kPerThread];
-    stage_offsets<D>(o0, pb, lst[0], tid);
-    stage_load<D>(kS, rk, o0);
-    stage_load<D>(vS, rv, o0);
-    stage_offsets<D>(offs_n, pb, lst[min(1, last)], tid);
-    j_n = lst[min(2, last)];
+    uint32_t o0[SH::kPerThread];
+    stage_offsets<D, 512>(o0, pb, uid(0), tid);
+    stage_load<D, 512>(kA, rk, o0);
+    stage_load<D, 512>(vA, rv, o0);
+    stage_offsets<D, 512>(o0, pb, uid(1), tid);
+    stage_load<D, 512>(kB, rk, o0);
+    stage_load<D, 512>(vB, rv, o0);
+    stage_store<D, 512>(kA, smem, tid);
+    stage_store<D, 512>(vA, smem + TL::kBytes, tid);
+    stage_offsets<D, 512>(o0, pb, uid(2), tid);
+    stage_load<D, 512>(kA, rk, o0);
+    stage_load<D, 512>(vA, rv, o0);
+    stage_offsets<D, 512>(offs_n, pb, uid(3), tid);
+    j_n = uid(4);
   }
 
-  for (int t = 0; t < cnt; ++t) {
-    __syncthreads();
-    stage_store<D>(kS, sk, tid);
-    stage_store<D>(vS, sv, tid);
-    __syncthreads();
-    int rows_n[Share<D>::kPerThread];
-    stage_rows<D>(rows_n, pb, j_n, tid);
-    pin_order();
-    stage_load<D>(kS, rk, offs_n);
-    stage_load<D>(vS, rv, offs_n);
-    pin_order();
-    j_n = lst[min(t + 3, last)];
-
+  auto compute_block = [&](const unsigned char* sk, const unsigned char* sv)
+                           __attribute__((always_inline)) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -391,12 +470,40 @@ __global__ __launch_bounds__(256, 2) void dq_bf16(
       dqa[mt] = mfma32(lds_tr8<D>(sk, r0, d0, j16), g0, dqa[mt]);
       dqa[mt] = mfma32(lds_tr8<D>(sk, r0 + 16, d0, j16), g1, dqa[mt]);
     }
-    rows_to_offsets<D>(offs_n, rows_n, tid);
+  };
+
+#define PRISM_DQ_STEP(T_, BUF_, KS_, VS_)                                   \
+  {                                                                         \
+    const int tt = (T_);                                                    \
+    __syncthreads();                                                        \
+    stage_store<D, 512>(KS_, smem + (1 - (BUF_)) * 2 * TL::kBytes, tid);    \
+    stage_store<D, 512>(VS_, smem + (1 - (BUF_)) * 2 * TL::kBytes +         \
+                                 TL::kBytes, tid);                          \
+    int rows_n[SH::kPerThread];                                             \
+    stage_rows<D, 512>(rows_n, pb, j_n, tid);                               \
+    pin_order();                                                            \
+    stage_load<D, 512>(KS_, rk, offs_n);                                    \
+    stage_load<D, 512>(VS_, rv, offs_n);                                    \
+    pin_order();                                                            \
+    j_n = uid(tt + 5);                                                      \
+    const uint32_t e = __builtin_amdgcn_readfirstlane(ulist[tt]);           \
+    if (e & mflag)                                                          \
+      compute_block(smem + (BUF_) * 2 * TL::kBytes,                         \
+                    smem + (BUF_) * 2 * TL::kBytes + TL::kBytes);           \
+    rows_to_offsets<D, 512>(offs_n, rows_n, tid);                           \
   }
 
-  // sum the two kh partials
+  int t = 0;
+  for (; t + 1 < ucnt; t += 2) {
+    PRISM_DQ_STEP(t, 0, kB, vB)
+    PRISM_DQ_STEP(t + 1, 1, kA, vA)
+  }
+  if (t < ucnt) PRISM_DQ_STEP(t, 0, kB, vB)
+#undef PRISM_DQ_STEP
+
+  // sum the two kh partials of each query half through LDS
   __syncthreads();
-  float* xch = reinterpret_cast<float*>(smem);
+  float* xch = reinterpret_cast<float*>(smem + half * 2 * TL::kBytes);
   if (kh == 1) {
 #pragma unroll
     for (int mt = 0; mt < DT; ++mt)
@@ -405,7 +512,7 @@ __global__ __launch_bounds__(256, 2) void dq_bf16(
         xch[((qh * 64 + lane) * DT + mt) * 16 + r] = dqa[mt][r];
   }
   __syncthreads();
-  if (kh == 0) {
+  if (kh == 0 && (half == 0 || has_second)) {
     float* dqr = dq + (head + qrow) * D;
 #pragma unroll
     for (int mt = 0; mt < DT; ++mt)
@@ -546,15 +653,17 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
   dim3 grid(Nb, Hh, B);
   if (dtype == PRISM_BF16) {
     const long long heads = (long long)B * Hh;
-    const dim3 g1(tiles::xcd_grid(Nb, heads));
-    const size_t dyn = 4 * tiles::Tile<D>::kBytes + 128 * sizeof(float) +
-                       8 * sizeof(int) + (size_t)Nb * sizeof(uint16_t);
-    PRISM_LAUNCH("dkdv_bf16", dkdv_bf16<D>, g1, dim3(256), dyn, stream,
+    const dim3 gp(tiles::xcd_grid((Nb + 1) / 2, heads));
+    const size_t dyn = 8 * tiles::Tile<D>::kBytes + 256 * sizeof(float) +
+                       (size_t)Nb * sizeof(uint16_t);
+    PRISM_LAUNCH("dkdv_bf16", dkdv_bf16<D>, gp, dim3(512), dyn, stream,
                  (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                  (const uint16_t*)d_o, lse, delta, perm, bits, words, Hh, N, heads,
                  scale, dk, dv);
     if ((st = check_launch("dkdv_bf16")) != PRISM_OK) return st;
-    PRISM_LAUNCH("dq_bf16", dq_bf16<D>, g1, dim3(256), 0, stream, (const uint16_t*)q,
+    const size_t dyn_q = 4 * tiles::Tile<D>::kBytes + 4 * (size_t)Nb +
+                         8 * (size_t)((Nb + 31) / 32);
+    PRISM_LAUNCH("dq_bf16", dq_bf16<D>, gp, dim3(512), dyn_q, stream, (const uint16_t*)q,
                  (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o,
                  lse, delta, perm, counts, kv_idx, capacity, Hh, N, heads, scale, dq);
     return check_launch("dq_bf16");

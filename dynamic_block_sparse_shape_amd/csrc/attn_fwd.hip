@@ -44,7 +44,6 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
   constexpr int KS = D / 16;     // k-steps of S^T = K Q^T
   constexpr int DT = D / 32;     // 32-row d tiles of O^T
   const int Nb = N / 64;
-  const int words = (Nb + 31) / 32;
   // two LDS buffers (K and V of one block each): block t+1 is published into
   // one while block t is read from the other -- one barrier per block.  Then
   // the union list (one entry per block: id | in-first << 16 |
@@ -74,48 +73,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
   const int32_t* lst0 = kv_idx + row0 * (long long)capacity;
   const int32_t* lst1 = lst0 + capacity;
 
-  // ---- ascending union of the two lists
-  for (int w = tid; w < 2 * words; w += 512) bits[w] = 0u;
-  __syncthreads();
-  for (int t = tid; t < cnt0; t += 512) {
-    const int j = lst0[t];
-    atomicOr(&bits[j >> 5], 1u << (j & 31));
-  }
-  for (int t = tid; t < cnt1; t += 512) {
-    const int j = lst1[t];
-    atomicOr(&bits[words + (j >> 5)], 1u << (j & 31));
-  }
-  __syncthreads();
-  int ucnt = 0;
-  {
-    // thread w owns bitmap word w (Nb <= 8192 = 32 * 256)
-    const uint32_t wa = tid < words ? bits[tid] : 0u;
-    const uint32_t wb = tid < words ? bits[words + tid] : 0u;
-    uint32_t wu = wa | wb;
-    const int n = __popc(wu);
-    int incl = n;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int x = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += x;
-    }
-    if (lane == 63) s_cnt[wave] = incl;
-    __syncthreads();
-    int pos = incl - n;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int x = s_cnt[w];
-      pos += w < wave ? x : 0;
-      ucnt += x;
-    }
-    while (wu) {
-      const int bit = __ffs(wu) - 1;
-      ulist[pos++] = (uint32_t)(tid * 32 + bit) | (((wa >> bit) & 1u) << 16) |
-                     (((wb >> bit) & 1u) << 17);
-      wu &= wu - 1u;
-    }
-  }
-  __syncthreads();
+  const int ucnt = pair_union(lst0, cnt0, lst1, cnt1, Nb, bits, ulist, s_cnt, tid);
 
   // a missing second block borrows the first one's rows (never written)
   const int iq = (half == 1 && has_second) ? i0 + 1 : i0;

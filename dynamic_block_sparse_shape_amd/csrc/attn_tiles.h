@@ -213,6 +213,59 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int s) {
   return as_bf16x8(u);
 }
 
+// Ascending union of two blocks' KV lists, built by a 512-thread workgroup.
+// Each entry is id | (in list 0) << 16 | (in list 1) << 17.  bits holds
+// 2 * ceil(Nb / 32) words and ulist Nb entries (LDS); s_cnt 8 ints.
+// Lists hold distinct ids in [0, Nb), Nb <= 8192.  Returns the union size;
+// ends with a barrier.
+__device__ __forceinline__ int pair_union(const int32_t* __restrict__ lst0,
+                                          int cnt0,
+                                          const int32_t* __restrict__ lst1,
+                                          int cnt1, int Nb, uint32_t* bits,
+                                          uint32_t* ulist, int* s_cnt, int tid) {
+  const int words = (Nb + 31) / 32;
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int w = tid; w < 2 * words; w += 512) bits[w] = 0u;
+  __syncthreads();
+  for (int t = tid; t < cnt0; t += 512) {
+    const int j = lst0[t];
+    atomicOr(&bits[j >> 5], 1u << (j & 31));
+  }
+  for (int t = tid; t < cnt1; t += 512) {
+    const int j = lst1[t];
+    atomicOr(&bits[words + (j >> 5)], 1u << (j & 31));
+  }
+  __syncthreads();
+  // thread w owns bitmap word w (words <= 256)
+  const uint32_t wa = tid < words ? bits[tid] : 0u;
+  const uint32_t wb = tid < words ? bits[words + tid] : 0u;
+  uint32_t wu = wa | wb;
+  const int n = __popc(wu);
+  int incl = n;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int x = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += x;
+  }
+  if (lane == 63) s_cnt[wave] = incl;
+  __syncthreads();
+  int pos = incl - n, ucnt = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int x = s_cnt[w];
+    pos += w < wave ? x : 0;
+    ucnt += x;
+  }
+  while (wu) {
+    const int bit = __ffs(wu) - 1;
+    ulist[pos++] = (uint32_t)(tid * 32 + bit) | (((wa >> bit) & 1u) << 16) |
+                   (((wb >> bit) & 1u) << 17);
+    wu &= wu - 1u;
+  }
+  __syncthreads();
+  return ucnt;
+}
+
 // Work item of this workgroup.  Workgroups are dealt round-robin to the 8
 // XCDs, so workgroup L runs on XCD L % 8.  Every head's Nb blocks are split
 // into 8 contiguous ranges, one per XCD, and heads are visited in order:
