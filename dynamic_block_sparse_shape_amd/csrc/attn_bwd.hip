@@ -205,6 +205,8 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
   // qbase(a) + b, qbase(a) = 32 qh + 16 (a / 2) + 8 hf + 4 (a % 2)
   const int arow = 32 * qh + slot_of(c);      // Q / dO row of this lane's M-row
   const uint32_t mflag = 1u << (13 + half);
+  RowAddr ra_q = row_addr<D>(arow, hf), ra_k = row_addr<D>(brow, hf);
+  TrAddr ta = tr_addr<D>(32 * qh, lane);
 
   // Q / dO tiles and one lse (tid < 64) or D (64 <= tid < 128) per thread
   // are staged one block ahead in registers and published into two LDS
@@ -255,10 +257,8 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32(lds_row8<D>(sq, arow, 2 * ks + hf),
-                 lds_row8<D>(skt, brow, 2 * ks + hf), s);
-      dp = mfma32(lds_row8<D>(sdo, arow, 2 * ks + hf),
-                  lds_row8<D>(svt, brow, 2 * ks + hf), dp);
+      s = mfma32(lds_row_at<D>(sq, ra_q, ks), lds_row_at<D>(skt, ra_k, ks), s);
+      dp = mfma32(lds_row_at<D>(sdo, ra_q, ks), lds_row_at<D>(svt, ra_k, ks), dp);
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
@@ -279,12 +279,10 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
     const bf16x8 g0 = pack8(dp, 0), g1 = pack8(dp, 1);
 #pragma unroll
     for (int mt = 0; mt < DT; ++mt) {
-      const int d0 = 32 * mt + 16 * (grp & 1);
-      const int r0 = 32 * qh + 8 * (grp >> 1);
-      dva[mt] = mfma32(lds_tr8<D>(sdo, r0, d0, j16), p0, dva[mt]);
-      dva[mt] = mfma32(lds_tr8<D>(sdo, r0 + 16, d0, j16), p1, dva[mt]);
-      dka[mt] = mfma32(lds_tr8<D>(sq, r0, d0, j16), g0, dka[mt]);
-      dka[mt] = mfma32(lds_tr8<D>(sq, r0 + 16, d0, j16), g1, dka[mt]);
+      dva[mt] = mfma32(lds_tr_at<D>(sdo, ta, 0, mt), p0, dva[mt]);
+      dva[mt] = mfma32(lds_tr_at<D>(sdo, ta, 1, mt), p1, dva[mt]);
+      dka[mt] = mfma32(lds_tr_at<D>(sq, ta, 0, mt), g0, dka[mt]);
+      dka[mt] = mfma32(lds_tr_at<D>(sq, ta, 1, mt), g1, dka[mt]);
     }
   };
 
@@ -310,6 +308,9 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
     xS = x_n;                                                               \
     j_n = uid(tt + 4);                                                      \
     const uint32_t e = __builtin_amdgcn_readfirstlane((uint32_t)ulist[tt]); \
+    opaque(ra_q);                                                           \
+    opaque(ra_k);                                                           \
+    opaque(ta);                                                             \
     if (e & mflag)                                                          \
       compute_block(sqo + (BUF_) * 2 * TL::kBytes, sx + (BUF_) * 128);      \
     rows_to_offsets<D, 512>(offs_n, rows_n, tid);                           \

@@ -107,6 +107,71 @@ __device__ __forceinline__ bf16x8 lds_tr8(const unsigned char* tile, int r0,
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Cheap per-lane addressing of the swizzled tiles.  With the XOR swizzle,
+// the address of row r, piece 2ks + hf is  y + ((ks << 5) ^ x)  for two lane
+// constants, and the transposed 4x4 reads of lds_tr8 at rows
+// rbase + 8 (grp / 2) + 16 a + (j / 4) (+4) and columns 32 mt + ... are
+// y_b + 16 a rows + ((mt << 6) ^ m_b)  (the swizzle of those rows does not
+// depend on a or rbase).  Kernels keep these 2 + 4 constants live instead of
+// one address register per fragment, and make them opaque once per loop
+// iteration so the compiler recomputes (one VALU op) rather than hoists.
+struct RowAddr {
+  uint32_t y, x;
+};
+template <int D>
+__device__ __forceinline__ RowAddr row_addr(int r, int hf) {
+  const int sw = Tile<D>::swz(r);
+  return {(uint32_t)(r * Tile<D>::kRowBytes + ((hf ^ (sw & 1)) << 4)),
+          (uint32_t)((sw & ~1) << 4)};
+}
+template <int D>
+__device__ __forceinline__ bf16x8 lds_row_at(const unsigned char* tile,
+                                            RowAddr a, int ks) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(
+      tile + (a.y + (((uint32_t)ks << 5) ^ a.x))));
+}
+
+struct TrAddr {
+  uint32_t y0, y1, m0, m1;
+};
+// rbase: first row of the 32-row half (multiple of 32); lane = lane id
+template <int D>
+__device__ __forceinline__ TrAddr tr_addr(int rbase, int lane) {
+  const int j = lane & 15, grp = lane >> 4;
+  const int x = 2 * (grp & 1) + ((j & 3) >> 1);
+  TrAddr t;
+  {
+    const int r = rbase + 8 * (grp >> 1) + (j >> 2);
+    const int sw = Tile<D>::swz(r);
+    t.y0 = (uint32_t)(r * Tile<D>::kRowBytes + (((x ^ sw) & 3) << 4) + 8 * (j & 1));
+    t.m0 = (uint32_t)((sw >> 2) << 6);
+  }
+  {
+    const int r = rbase + 8 * (grp >> 1) + (j >> 2) + 4;
+    const int sw = Tile<D>::swz(r);
+    t.y1 = (uint32_t)(r * Tile<D>::kRowBytes + (((x ^ sw) & 3) << 4) + 8 * (j & 1));
+    t.m1 = (uint32_t)((sw >> 2) << 6);
+  }
+  return t;
+}
+// Same fragment as lds_tr8(tile, rbase + 8 (grp / 2) + 16 a, 32 mt + 16 (grp & 1), j)
+template <int D>
+__device__ __forceinline__ bf16x8 lds_tr_at(const unsigned char* tile, TrAddr t,
+                                           int a, int mt) {
+  const uint32_t ro = (uint32_t)(16 * a * Tile<D>::kRowBytes);
+  lds_bf16x4* p0 = (lds_bf16x4*)(tile + (t.y0 + ro + (((uint32_t)mt << 6) ^ t.m0)));
+  lds_bf16x4* p1 = (lds_bf16x4*)(tile + (t.y1 + ro + (((uint32_t)mt << 6) ^ t.m1)));
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+__device__ __forceinline__ void opaque(RowAddr& a) {
+  asm volatile("" : "+v"(a.y), "+v"(a.x));
+}
+__device__ __forceinline__ void opaque(TrAddr& t) {
+  asm volatile("" : "+v"(t.y0), "+v"(t.y1), "+v"(t.m0), "+v"(t.m1));
+}
+
 // Global -> register staging of one 64-row tile.  Rows are gathered with
 // buffer loads: one resource per (tensor, head) and 32-bit byte offsets that
 // the K and V (or Q and dO) tiles of a block share.
