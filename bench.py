@@ -127,22 +127,32 @@ def cpu_baseline(x, w, counts_host, perm_host, budget_s):
         threads = os.cpu_count() or 1
 
     def widen(a):
-        return bf16_bits_to_f32(a).astype(np.float64)
+        if a.dtype == np.uint16:
+            return bf16_bits_to_f32(a).astype(np.float64)
+        return a.astype(np.float64)
 
     cfg = x.cfg
     T, H, W = cfg["T"], cfg["H"], cfg["W"]
     zones = po.zone_tiling(T, H, W)
-    F = x.feat[0].reshape(T, H, W, -1)
-    A = x.a2v[0].reshape(T, H, W, -1)
-    # stage 1: a few full zones
-    nz = 6
-    t0 = time.perf_counter()
-    for (o, e) in zones[:nz]:
-        sl = (slice(o[0], o[0] + e[0]), slice(o[1], o[1] + e[1]),
-              slice(o[2], o[2] + e[2]))
-        st = po.zone_statistics(widen(F[sl]), widen(A[sl]))
-        po.choose_shape(st, e)
-    t_stage1 = (time.perf_counter() - t0) / nz * len(zones) * w["B"]
+    if x.feat is not None:
+        # stage 1: a few full zones
+        F = x.feat[0].reshape(T, H, W, -1)
+        A = x.a2v[0].reshape(T, H, W, -1)
+        nz = min(6, len(zones))
+        t0 = time.perf_counter()
+        for (o, e) in zones[:nz]:
+            sl = (slice(o[0], o[0] + e[0]), slice(o[1], o[1] + e[1]),
+                  slice(o[2], o[2] + e[2]))
+            st = po.zone_statistics(widen(F[sl]), widen(A[sl]))
+            po.choose_shape(st, e)
+        t_stage1 = (time.perf_counter() - t0) / nz * len(zones) * w["B"]
+        s1 = f"stage 1 on {nz} of {len(zones)} zones"
+    else:
+        # fixed shape: stage 1 is the permutation alone
+        t0 = time.perf_counter()
+        po.block_permutation(T, H, W, zones, [cfg["fixed_shape"]] * len(zones))
+        t_stage1 = (time.perf_counter() - t0) * w["B"]
+        s1 = "stage 1 (fixed-shape permutation) in full"
     # stages 2-3: one whole head
     perm = perm_host[0]
     q0, k0 = widen(x.q[0, 0]), widen(x.k[0, 0])
@@ -153,7 +163,7 @@ def cpu_baseline(x, w, counts_host, perm_host, budget_s):
     # each, as the oracle would run the whole head)
     v0, do0 = widen(x.v[0, 0]), widen(x.do[0, 0])
     rng = np.random.default_rng(0)
-    used = 16
+    used = min(16, w["Nb"])
     sample = sorted(rng.choice(w["Nb"], size=used, replace=False).tolist())
     pairs = int(sum(int(route["counts"][i]) for i in sample))
     t0 = time.perf_counter()
@@ -169,7 +179,7 @@ def cpu_baseline(x, w, counts_host, perm_host, budget_s):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 numpy oracle: stage 1 on {nz} of {len(zones)} zones, "
+        "sample": (f"fp64 numpy oracle: {s1}, "
                    f"stages 2-3 on 1 of {w['Hh']} heads, attention fwd+bwd on "
                    f"{used} query blocks ({pairs} selected pairs) of head 0; "
                    f"extrapolated to the whole step: {total:.1f} s"),

@@ -168,7 +168,10 @@ prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
  * q, k, v : [B, Hh, N, d] dtype (bf16: MFMA path with fp32 accumulation;
  *           fp32: reference-precision path).
  * perm, counts, kv_idx, capacity : from stages 1 and 3.  Every count must be
- *           in [1, Nb] and every listed id in [0, Nb) (caller's contract).
+ *           in [1, Nb], every listed id in [0, Nb) and the ids of one row
+ *           distinct, in any order (caller's contract; stage 3 output
+ *           satisfies it).  Neighbouring query blocks (2p, 2p+1) are
+ *           processed together over the union of their lists.
  * softmax_scale : <= 0 means 1/sqrt(d).
  * o   : out [B, Hh, N, d] dtype, raster order.
  * lse : out [B, Hh, N] fp32, natural-log logsumexp of the scaled scores.
