@@ -202,7 +202,7 @@ def _random_lists(nb, rng, maxc=None):
     counts = np.empty(nb, dtype=np.int64)
     lists = []
     for i in range(nb):
-        c = int(rng.integers(1, (maxc or nb) + 1))
+        c = int(rng.integers(1, min(maxc or nb, nb) + 1))
         if i == 0:
             c = nb                      # one full row
         if i == 1:
@@ -283,6 +283,34 @@ def test_stage4_backward(dtype, d):
             for name, g, r in zip(("dq", "dk", "dv"), got, ref):
                 st = assert_close(g[b, h], r, bf, f"{name}[{b},{h}]")
                 _print(" ", name, st)
+
+
+@pytest.mark.parametrize("grid", [(4, 4, 4), (4, 4, 8), (4, 4, 12)])
+@pytest.mark.parametrize("d", [128, 64])
+def test_stage4_tiny_block_counts(grid, d):
+    """1, 2 and 3 blocks: a pair with no second block, one full pair, and a
+    pair plus a single (neighbouring blocks are processed in pairs)."""
+    T, H, W = grid
+    c = _attn_case("bf16", d, T=T, H=H, W=W, B=2, Hh=2, seed=11)
+    _print("tiny", grid, d)
+    args = [to_dev(c[n]) for n in ("q", "k", "v")]
+    perm, counts, kv = to_dev(c["perm"]), to_dev(c["counts"]), to_dev(c["kv"])
+    o, lse = P.sparse_attn_fwd(*args, perm, counts, kv)
+    dq, dk, dv = P.sparse_attn_bwd(*args, o, to_dev(c["do"]), lse, perm,
+                                   counts, kv)
+    torch.cuda.synchronize()
+    o, lse = to_host(o), lse.cpu().numpy()
+    got = [t.cpu().numpy() for t in (dq, dk, dv)]
+    for b in range(c["B"]):
+        for h in range(c["Hh"]):
+            qq, kk, vv = (widen(c[n][b, h]) for n in ("q", "k", "v"))
+            ro, rl = po.sparse_attn_fwd(qq, kk, vv, c["perm"][b], c["lists"][b][h])
+            assert_close(o[b, h], ro, True, f"o[{b},{h}]")
+            assert_close(lse[b, h], rl, True, f"lse[{b},{h}]")
+            ref = po.sparse_attn_bwd(qq, kk, vv, widen(c["do"][b, h]),
+                                     c["perm"][b], c["lists"][b][h])
+            for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+                assert_close(g[b, h], r, True, f"{name}[{b},{h}]")
 
 
 def test_stage4_deterministic_and_poison_safe():
