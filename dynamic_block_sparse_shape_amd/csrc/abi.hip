@@ -106,6 +106,15 @@ static prism_status check_zone_kinds(const ZoneGeom& g, int fixed_shape) {
   return PRISM_OK;
 }
 
+// Tensors are read and written with 16-byte vector accesses; index arrays
+// and lse with 4-byte ones.
+static bool aligned(const void* p, uintptr_t a) {
+  return p == nullptr || (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+#define PRISM_CHECK_ALIGNED(p, a)                                         \
+  PRISM_CHECK(aligned((p), (a)), PRISM_ERR_INVALID_ARG,                   \
+              "%s must be %d-byte aligned", #p, (int)(a))
+
 static prism_status check_heads(int B, int Hh, int N, int d) {
   PRISM_CHECK(B >= 1 && Hh >= 1 && N >= 1 && d >= 1, PRISM_ERR_INVALID_ARG,
               "sizes must be >= 1 (B=%d Hh=%d N=%d d=%d)", B, Hh, N, d);
@@ -205,6 +214,13 @@ prism_status prism_zone_shapes(const void* feat, const void* a2v_res,
               fixed_shape);
   PRISM_CHECK(zone_shape && perm, PRISM_ERR_INVALID_ARG,
               "zone_shape and perm must not be NULL");
+  PRISM_CHECK_ALIGNED(feat, 16);
+  PRISM_CHECK_ALIGNED(a2v_res, 16);
+  PRISM_CHECK_ALIGNED(workspace, 16);
+  PRISM_CHECK_ALIGNED(zone_stats, 8);
+  PRISM_CHECK_ALIGNED(zone_shape, 4);
+  PRISM_CHECK_ALIGNED(perm, 4);
+  PRISM_CHECK_ALIGNED(inv_perm, 4);
   st = check_zone_kinds(g, fixed_shape);
   if (st != PRISM_OK) return st;
   if (fixed_shape < 0) {
@@ -239,6 +255,12 @@ prism_status prism_pool_blocks(const void* q, const void* k, int dtype,
   PRISM_CHECK(dtype_ok(dtype), PRISM_ERR_INVALID_ARG, "bad dtype %d", dtype);
   PRISM_CHECK(q && k && perm && q_mean && k_mean && proxy,
               PRISM_ERR_INVALID_ARG, "null pointer argument");
+  PRISM_CHECK_ALIGNED(q, 16);
+  PRISM_CHECK_ALIGNED(k, 16);
+  PRISM_CHECK_ALIGNED(q_mean, 16);
+  PRISM_CHECK_ALIGNED(k_mean, 16);
+  PRISM_CHECK_ALIGNED(proxy, 16);
+  PRISM_CHECK_ALIGNED(perm, 4);
   const int Nb = N / PRISM_BLOCK_TOKENS;
   PRISM_CHECK(Nb <= 8192, PRISM_ERR_UNSUPPORTED, "Nb=%d above 8192", Nb);
   return launch_pool_proxy(q, k, dtype, perm, B, Hh, N, d, q_mean, k_mean,
@@ -254,6 +276,9 @@ prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
               "sizes must be >= 1 (B=%d Hh=%d Nb=%d)", B, Hh, Nb);
   PRISM_CHECK(proxy && counts && kv_idx, PRISM_ERR_INVALID_ARG,
               "null pointer argument");
+  PRISM_CHECK_ALIGNED(proxy, 8);
+  PRISM_CHECK_ALIGNED(counts, 4);
+  PRISM_CHECK_ALIGNED(kv_idx, 4);
   PRISM_CHECK(top_k >= 0, PRISM_ERR_INVALID_ARG, "top_k=%d must be >= 0",
               top_k);
   PRISM_CHECK(cdf_threshold >= 0.0 && cdf_threshold <= 1.0,
@@ -283,6 +308,12 @@ static prism_status check_attn_common(const void* q, const void* k,
   PRISM_CHECK(dtype_ok(dtype), PRISM_ERR_INVALID_ARG, "bad dtype %d", dtype);
   PRISM_CHECK(q && k && v && perm && counts && kv_idx, PRISM_ERR_INVALID_ARG,
               "null pointer argument");
+  PRISM_CHECK_ALIGNED(q, 16);
+  PRISM_CHECK_ALIGNED(k, 16);
+  PRISM_CHECK_ALIGNED(v, 16);
+  PRISM_CHECK_ALIGNED(perm, 4);
+  PRISM_CHECK_ALIGNED(counts, 4);
+  PRISM_CHECK_ALIGNED(kv_idx, 4);
   PRISM_CHECK(capacity >= N / PRISM_BLOCK_TOKENS, PRISM_ERR_SHAPE,
               "capacity=%d < Nb=%d", capacity, N / PRISM_BLOCK_TOKENS);
   PRISM_CHECK(isfinite(softmax_scale), PRISM_ERR_INVALID_ARG,
@@ -303,6 +334,8 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k,
                                       capacity, B, Hh, N, d, softmax_scale);
   if (st != PRISM_OK) return st;
   PRISM_CHECK(o && lse, PRISM_ERR_INVALID_ARG, "null output pointer");
+  PRISM_CHECK_ALIGNED(o, 16);
+  PRISM_CHECK_ALIGNED(lse, 4);
   float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
   return launch_attn_fwd(q, k, v, dtype, perm, counts, kv_idx, capacity, B,
                          Hh, N, d, scale, o, lse, (hipStream_t)stream);
@@ -329,6 +362,13 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k,
   if (st != PRISM_OK) return st;
   PRISM_CHECK(o && d_o && lse && dq && dk && dv, PRISM_ERR_INVALID_ARG,
               "null pointer argument");
+  PRISM_CHECK_ALIGNED(o, 16);
+  PRISM_CHECK_ALIGNED(d_o, 16);
+  PRISM_CHECK_ALIGNED(lse, 4);
+  PRISM_CHECK_ALIGNED(dq, 16);
+  PRISM_CHECK_ALIGNED(dk, 16);
+  PRISM_CHECK_ALIGNED(dv, 16);
+  PRISM_CHECK_ALIGNED(workspace, 16);
   size_t need = attn_bwd_ws_bytes(B, Hh, N, d);
   PRISM_CHECK(workspace != nullptr && workspace_bytes >= need,
               PRISM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",

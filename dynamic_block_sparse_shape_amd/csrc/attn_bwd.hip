@@ -37,20 +37,33 @@ __device__ __forceinline__ float ld<float>(const float* p) {
   return *p;
 }
 
-// D_r = <dO_r, O_r>, one row per 16 lanes... generic: one thread-group of
-// D/8 lanes per row for bf16, plain loop for fp32.
+// D_r = <dO_r, O_r>: each thread takes one 16-byte piece of the row of O and
+// of dO (8 bf16 or 4 fp32), a group of D*sizeof(E)/16 lanes reduces a row.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_delta(const E* __restrict__ o,
                                                  const E* __restrict__ d_o,
                                                  long long rows,
                                                  float* __restrict__ delta) {
-  constexpr int TPR = 16;  // threads per row
+  constexpr int PER = 16 / (int)sizeof(E);   // elements per 16-byte piece
+  constexpr int TPR = D / PER;               // threads per row (<= 64)
   const long long r = (long long)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
   const int part = threadIdx.x % TPR;
   float s = 0.f;
   if (r < rows) {
-    for (int e = part; e < D; e += TPR)
-      s += ld<E>(o + r * D + e) * ld<E>(d_o + r * D + e);
+    const uint4 a = *reinterpret_cast<const uint4*>(o + r * D + part * PER);
+    const uint4 g = *reinterpret_cast<const uint4*>(d_o + r * D + part * PER);
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w};
+    const uint32_t gv[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (sizeof(E) == 2) {
+        s += __uint_as_float(av[t] << 16) * __uint_as_float(gv[t] << 16);
+        s += __uint_as_float(av[t] & 0xffff0000u) *
+             __uint_as_float(gv[t] & 0xffff0000u);
+      } else {
+        s += __uint_as_float(av[t]) * __uint_as_float(gv[t]);
+      }
+    }
   }
 #pragma unroll
   for (int off = TPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
@@ -633,14 +646,17 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
   uint32_t* bits = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + dbytes);
   const long long nbits = (long long)B * Hh * Nb * words;
 
-  if (dtype == PRISM_BF16)
-    PRISM_LAUNCH("bwd_delta", (bwd_delta<uint16_t, D>), dim3((unsigned)((rows + 15) / 16)),
-                       dim3(256), 0, stream, (const uint16_t*)o, (const uint16_t*)d_o,
-                       rows, delta);
-  else
-    PRISM_LAUNCH("bwd_delta", (bwd_delta<float, D>), dim3((unsigned)((rows + 15) / 16)),
-                       dim3(256), 0, stream, (const float*)o, (const float*)d_o, rows,
-                       delta);
+  if (dtype == PRISM_BF16) {
+    const long long rpb = 256 / (D / 8);      // rows per block
+    PRISM_LAUNCH("bwd_delta", (bwd_delta<uint16_t, D>),
+                 dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream,
+                 (const uint16_t*)o, (const uint16_t*)d_o, rows, delta);
+  } else {
+    const long long rpb = 256 / (D / 4);
+    PRISM_LAUNCH("bwd_delta", (bwd_delta<float, D>),
+                 dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream,
+                 (const float*)o, (const float*)d_o, rows, delta);
+  }
   prism_status st = check_launch("bwd_delta");
   if (st != PRISM_OK) return st;
   const unsigned cg = (unsigned)std::min<long long>((nbits + 255) / 256, 65535);

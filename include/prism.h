@@ -30,6 +30,10 @@
  *  - Token layout is raster order t*H*W + h*W + w.  Per-head tensors are
  *    [B, Hh, N, d] contiguous; block-ordered data is reached through `perm`
  *    (the caller never permutes tensors).
+ *  - Float tensors (bf16 / fp32 / fp64) and workspaces must be 16-byte
+ *    aligned (they are read and written with 16-byte vector accesses);
+ *    int32 arrays, lse and zone_stats need their natural alignment.  A
+ *    misaligned pointer is rejected with PRISM_ERR_INVALID_ARG.
  *  - Blocks always hold 64 tokens, so Nb = N / 64.
  *  - Calls that share a workspace or outputs must not overlap in time.
  */
@@ -45,7 +49,7 @@ extern "C" {
 
 typedef enum {
   PRISM_OK = 0,
-  PRISM_ERR_INVALID_ARG = 1, /* null pointer, size < 1, bad dtype, k < 0, ... */
+  PRISM_ERR_INVALID_ARG = 1, /* null / misaligned pointer, size < 1, bad dtype, ... */
   PRISM_ERR_SHAPE = 2,       /* inconsistent sizes, zone without a legal shape */
   PRISM_ERR_UNSUPPORTED = 3, /* head_dim / dtype combination not built        */
   PRISM_ERR_WORKSPACE = 4,   /* workspace missing or too small                */

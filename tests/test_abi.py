@@ -124,3 +124,30 @@ def test_attention_rejections():
     _expect(4, P.prism_sparse_attn_bwd, *(bwd[:19] + [None] + bwd[20:]))
     _expect(1, P.prism_sparse_attn_bwd, *(bwd[:4] + [None] + bwd[5:]))
     _expect(3, P.prism_sparse_attn_bwd, *(bwd[:14] + [32] + bwd[15:]))
+
+
+def test_misaligned_pointers_rejected():
+    """Tensors are accessed with 16-byte vectors: misaligned pointers are
+    refused before any HIP call."""
+    zs = dict(feat=FAKE + 8, a2v_res=FAKE, dtype=1, B=1, T=20, H=68, W=120,
+              C=3072, zone_t=8, zone_h=8, zone_w=8, lambda_a2v=1.0,
+              fixed_shape=-1, zone_shape=FAKE, perm=FAKE, inv_perm=None,
+              zone_stats=None, workspace=FAKE, workspace_bytes=1 << 40,
+              stream=None)
+    _expect(1, P.prism_zone_shapes, *zs.values())
+    zs.update(feat=FAKE, perm=FAKE + 2)
+    _expect(1, P.prism_zone_shapes, *zs.values())
+    _expect(1, P.prism_pool_blocks, FAKE + 4, FAKE, 1, FAKE, 1, 2, 256, 64,
+            FAKE, FAKE, FAKE, None)
+    _expect(1, P.prism_pool_blocks, FAKE, FAKE, 1, FAKE, 1, 2, 256, 64,
+            FAKE, FAKE, FAKE + 8, None)
+    _expect(1, P.prism_select_blocks, FAKE, 1, 2, 4, 1, 0.2, FAKE + 2, FAKE,
+            4, None)
+    base = [FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 4, 1, 2, 256, 128, -1.0,
+            FAKE, FAKE, None, 0, None]
+    _expect(1, P.prism_sparse_attn_fwd, *([FAKE + 8] + base[1:]))
+    _expect(1, P.prism_sparse_attn_fwd, *(base[:13] + [FAKE + 8] + base[14:]))
+    bwd = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 4, 1, 2,
+           256, 128, -1.0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    _expect(1, P.prism_sparse_attn_bwd, *(bwd[:16] + [FAKE + 4] + bwd[17:]))
+    _expect(1, P.prism_sparse_attn_bwd, *(bwd[:19] + [FAKE + 8] + bwd[20:]))
