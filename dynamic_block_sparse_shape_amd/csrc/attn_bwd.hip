@@ -8,15 +8,16 @@
 //
 // Launch sequence (deterministic, no floating-point atomics):
 //   bwd_delta       D_r per query row (fp32).
-//   bitmap_clear /  column bitmaps: bit i of KV block j's word set when query
-//   bitmap_build    block i selected j -- the KV->query lists, read in
-//                   ascending i by the dK/dV kernel.
-//   dkdv_bf16       one workgroup per KV block; loops over the query blocks
-//                   that selected it.
-//   dq_bf16         one workgroup per query block; loops over its list.
+//   bitmap_build    word-major column bitmaps: bit i of KV block j's word
+//                   set when query block i selected j -- the KV->query
+//                   lists, read in ascending i by the dK/dV kernel.
+//   dkdv_bf16       one workgroup per pair of neighbouring KV blocks; loops
+//                   over the union of the query blocks that selected them.
+//   dq_bf16         one workgroup per pair of neighbouring query blocks;
+//                   loops over the union of their lists.
 // Both use v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulation, row-major
 // swizzled LDS tiles with transposed fragments from ds_read_b64_tr_b16, and
-// two-deep register prefetch (see attn_tiles.h); the fp32 dtype uses plain
+// register-staged gathers (see attn_tiles.h); the fp32 dtype uses plain
 // per-thread kernels with the same structure.
 #include <algorithm>
 
@@ -70,28 +71,31 @@ __global__ __launch_bounds__(256) void bwd_delta(const E* __restrict__ o,
   if (r < rows && part == 0) delta[r] = s;
 }
 
-__global__ void bitmap_clear(uint32_t* __restrict__ bits, long long n) {
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (long long)gridDim.x * blockDim.x)
-    bits[i] = 0u;
-}
-
-// bit i of word (j, i / 32) <- query block i selected KV block j
-__global__ void bitmap_build(const int32_t* __restrict__ counts,
-                             const int32_t* __restrict__ kv_idx, int capacity,
-                             int Nb, int words, long long rows,
-                             uint32_t* __restrict__ bits) {
-  const long long row = (long long)blockIdx.x * 4 + threadIdx.x / 64;
-  if (row >= rows) return;
-  const int lane = threadIdx.x % 64;
-  const long long bh = row / Nb;
-  const int i = (int)(row % Nb);
-  const int cnt = counts[row];
-  const int32_t* lst = kv_idx + row * (long long)capacity;
-  for (int t = lane; t < cnt; t += 64) {
-    const int j = lst[t];
-    atomicOr(&bits[(bh * Nb + j) * words + (i >> 5)], 1u << (i & 31));
+// Column bitmaps of the selection, word-major: bits[(bh * words + w) * Nb + j]
+// holds bit i - 32 w for every query block i in [32 w, 32 w + 32) that
+// selected KV block j.  One workgroup per (bh, w) ORs its 32 lists into an
+// LDS row of Nb words and writes the row out whole (no global atomics, no
+// clearing pass).
+__global__ __launch_bounds__(256) void bitmap_build(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ kv_idx,
+    int capacity, int Nb, int words, uint32_t* __restrict__ bits) {
+  extern __shared__ uint32_t srow[];                      // [Nb]
+  const long long bh = blockIdx.y;
+  const int w = blockIdx.x;
+  for (int j = threadIdx.x; j < Nb; j += 256) srow[j] = 0u;
+  __syncthreads();
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  for (int r = wave; r < 32; r += 4) {
+    const int i = 32 * w + r;
+    if (i >= Nb) break;
+    const long long row = bh * Nb + i;
+    const int cnt = counts[row];
+    const int32_t* lst = kv_idx + row * (long long)capacity;
+    for (int t = lane; t < cnt; t += 64) atomicOr(&srow[lst[t]], 1u << r);
   }
+  __syncthreads();
+  uint32_t* out = bits + (bh * words + w) * (long long)Nb;
+  for (int j = threadIdx.x; j < Nb; j += 256) out[j] = srow[j];
 }
 
 // ------------------------------------------------------- dK / dV (bf16)
@@ -145,9 +149,9 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
   // ---- ascending union of the two columns (thread w owns word w)
   int ucnt = 0;
   {
-    const uint32_t* col0 = bits + (bh * Nb + j0) * words;
-    const uint32_t wa = tid < words ? col0[tid] : 0u;
-    const uint32_t wb = (tid < words && has_second) ? col0[words + tid] : 0u;
+    const uint32_t* col0 = bits + (bh * words + tid) * (long long)Nb + j0;
+    const uint32_t wa = tid < words ? col0[0] : 0u;
+    const uint32_t wb = (tid < words && has_second) ? col0[1] : 0u;
     uint32_t wu = wa | wb;
     const int n = __popc(wu);
     int incl = n;
@@ -599,9 +603,9 @@ __global__ __launch_bounds__(64) void dkdv_f32(
   float ak[D], av[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) ak[e] = av[e] = 0.f;
-  const uint32_t* col = bits + (((long long)b * Hh + h) * Nb + j) * words;
+  const uint32_t* col = bits + ((long long)b * Hh + h) * words * (long long)Nb + j;
   for (int w = 0; w < words; ++w) {
-    uint32_t word = col[w];
+    uint32_t word = col[(long long)w * Nb];
     while (word) {
       const int i = w * 32 + __ffs(word) - 1;
       word &= word - 1;
@@ -644,7 +648,6 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
   float* delta = static_cast<float*>(ws);
   const size_t dbytes = ((rows * sizeof(float) + 255) / 256) * 256;
   uint32_t* bits = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + dbytes);
-  const long long nbits = (long long)B * Hh * Nb * words;
 
   if (dtype == PRISM_BF16) {
     const long long rpb = 256 / (D / 8);      // rows per block
@@ -659,12 +662,9 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
   }
   prism_status st = check_launch("bwd_delta");
   if (st != PRISM_OK) return st;
-  const unsigned cg = (unsigned)std::min<long long>((nbits + 255) / 256, 65535);
-  PRISM_LAUNCH("bitmap_clear", bitmap_clear, dim3(cg), dim3(256), 0, stream, bits, nbits);
-  if ((st = check_launch("bitmap_clear")) != PRISM_OK) return st;
-  const long long qrows = (long long)B * Hh * Nb;
-  PRISM_LAUNCH("bitmap_build", bitmap_build, dim3((unsigned)((qrows + 3) / 4)), dim3(256), 0,
-                     stream, counts, kv_idx, capacity, Nb, words, qrows, bits);
+  PRISM_LAUNCH("bitmap_build", bitmap_build, dim3((unsigned)words, (unsigned)(B * Hh)),
+               dim3(256), (size_t)Nb * sizeof(uint32_t), stream, counts, kv_idx,
+               capacity, Nb, words, bits);
   if ((st = check_launch("bitmap_build")) != PRISM_OK) return st;
 
   dim3 grid(Nb, Hh, B);
