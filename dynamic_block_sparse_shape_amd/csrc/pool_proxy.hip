@@ -102,15 +102,32 @@ __global__ __launch_bounds__(kThreads) void proxy_logits(
 #pragma unroll
     for (int c = 0; c < 2; ++c) acc[a][c] = f64x4{0.0, 0.0, 0.0, 0.0};
 
-  for (int k0 = 0; k0 < d; k0 += kKs) {
-    // stage 64 x 32 doubles of each operand (row-major, padded)
-    for (int e = threadIdx.x; e < kTile * kKs; e += kThreads) {
-      const int r = e / kKs, c = e % kKs;
+  // each thread holds 8 doubles of each operand's next k-slice in registers
+  // (rows r = tid / 32 + 8 u, column tid % 32): the global loads of slice
+  // k0 + 32 are in flight while slice k0 is multiplied from LDS
+  constexpr int kPer = kTile * kKs / kThreads;   // 8
+  double ra[kPer], rb[kPer];
+  const int rc = threadIdx.x % kKs, rr = threadIdx.x / kKs;
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int r = rr + (kThreads / kKs) * u;
       const int gi = ti * kTile + r, gj = tj * kTile + r;
-      As[r * kLd + c] = gi < Nb ? Q[(long long)gi * d + k0 + c] : 0.0;
-      Bs[r * kLd + c] = gj < Nb ? K[(long long)gj * d + k0 + c] : 0.0;
+      ra[u] = gi < Nb ? Q[(long long)gi * d + k0 + rc] : 0.0;
+      rb[u] = gj < Nb ? K[(long long)gj * d + k0 + rc] : 0.0;
+    }
+  };
+  load(0);
+  for (int k0 = 0; k0 < d; k0 += kKs) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int r = rr + (kThreads / kKs) * u;
+      As[r * kLd + rc] = ra[u];
+      Bs[r * kLd + rc] = rb[u];
     }
     __syncthreads();
+    if (k0 + kKs < d) load(k0 + kKs);
 #pragma unroll
     for (int kk = 0; kk < kKs; kk += 4) {
       double a[2], bb[2];
@@ -126,7 +143,6 @@ __global__ __launch_bounds__(kThreads) void proxy_logits(
         for (int n = 0; n < 2; ++n)
           acc[m][n] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[m], bb[n], acc[m][n], 0, 0, 0);
     }
-    __syncthreads();
   }
   double* Z = z + (long long)bh * Nb * Nb;
 #pragma unroll
@@ -182,10 +198,11 @@ __global__ __launch_bounds__(kThreads) void row_softmax(double* __restrict__ p,
   if (lane == 0) red[wave] = s;
   __syncthreads();
   s = (red[0] + red[1]) + (red[2] + red[3]);
+  const double inv_s = 1.0 / s;     // within 1 ulp of dividing each entry
 #pragma unroll
   for (int e = 0; e < NPT; ++e) {
     const int j = threadIdx.x + e * kThreads;
-    if (j < Nb) row[j] = x[e] / s;
+    if (j < Nb) row[j] = x[e] * inv_s;
   }
 }
 
