@@ -8,8 +8,12 @@
 //     - transposed-operand reads: ds_read_b64_tr_b16 (gfx950), where each
 //       quarter-wave reads 8 bytes from 4 consecutive rows x 4 columns and
 //       the hardware hands every lane 4 consecutive rows of one column.
-// * A workgroup of 256 threads stages a tile with 16-byte global loads held
-//   in registers (two blocks ahead), then one ds_write_b128 per piece.
+// * A workgroup (256 or 512 threads) gathers a tile's rows through the
+//   token permutation with 16-byte buffer loads held in registers one or two
+//   blocks ahead, then publishes it with one ds_write_b128 per piece.
+// * Neighbouring blocks are processed in pairs over the union of their block
+//   lists (pair_union), and work items are ordered head by head across the 8
+//   XCDs (xcd_item).
 // * MFMA v_mfma_f32_32x32x16_bf16 operand layouts (lane l, c = l % 32,
 //   h = l / 32): A[i][k] holds i = c, k = 8h .. 8h+7; B[k][j] holds j = c,
 //   k = 8h .. 8h+7; C[i][j] holds j = c and rows i = 8a + 4h + b in register
@@ -334,8 +338,8 @@ __device__ __forceinline__ int pair_union(const int32_t* __restrict__ lst0,
 // Work item of this workgroup.  Workgroups are dealt round-robin to the 8
 // XCDs, so workgroup L runs on XCD L % 8.  Every head's Nb blocks are split
 // into 8 contiguous ranges, one per XCD, and heads are visited in order:
-// all XCDs work on the same head at the same time (its K / V, ~150 MB at
-// the 2K grid, stays in the MALL) and each XCD's L2 sees neighbouring
+// all XCDs work on the same head at the same time (one head's K / V, ~150 MB
+// at the 2K grid, is the whole working set) and each XCD's L2 sees neighbouring
 // blocks, whose block lists overlap.  Returns false for padding items.
 __device__ __forceinline__ bool xcd_item(int Nb, long long heads, long long& bh,
                                          int& i) {
