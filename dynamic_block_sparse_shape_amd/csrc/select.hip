@@ -9,10 +9,12 @@
 // One workgroup per proxy row; the row (<= 8192 fp64) lives in registers.
 //  1. Windowed radix refinement on the fp64 bit patterns (non-negative
 //     doubles order like unsigned integers).  Each pass buckets the keys of
-//     the current band [lo, hi] by 255 - min(255, (hi >> s) - (key >> s)):
-//     the first pass (s = 48: 16 buckets per octave, 16 octaves below the
-//     row maximum) already spreads a softmax row well; later passes take 8
-//     more bits.  Per-bucket counts and approximate masses in LDS locate the
+//     a window at the top of the current band into 256 buckets of 2^s keys:
+//     the first window is an eighth of an octave around the row mean (a
+//     near-flat softmax row keeps most keys there); when the crossing lies
+//     outside it the search continues with 16 buckets per octave below the
+//     band's largest key, and each later pass takes 8 more bits.  Per-bucket
+//     counts and approximate masses in LDS locate the
 //     bucket where the count reaches max(k, 1) and the mass exceeds the
 //     threshold by a safety margin far above any summation-order error;
 //     everything above it is selected, the search continues inside it.
@@ -42,8 +44,8 @@ constexpr int kBand = 64;          // band size for the one-wave fast path
 constexpr double kMassMargin = 1e-11;  // >> (n + 64) * 2^-53 for n <= 8192
 
 struct SelShared {
-  int hcnt[256];
-  double hmass[256];
+  int hcnt[2][256];          // two histograms: one is cleared while the
+  double hmass[2][256];      // other is filled
   unsigned long long ckey[kSortCap];
   int cidx[kSortCap];
   unsigned bits[kThreads];   // 8192 bits: one word per thread
@@ -101,6 +103,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_rows(
     sh.wmax[wave] = kmax;
   }
   sh.bits[tid] = 0u;
+  sh.hcnt[0][tid] = 0;
+  sh.hmass[0][tid] = 0.0;
   __syncthreads();
   total = (sh.wsum[0] + sh.wsum[1]) + (sh.wsum[2] + sh.wsum[3]);
   {
@@ -127,24 +131,29 @@ __global__ __launch_bounds__(kThreads, 4) void select_rows(
     // (cnt_above, mass_above) and keys below lo are not.  Each pass
     // histograms the window [wlo, whi] at the band's top, 256 buckets of
     // 2^s keys, counts keys in (whi, hi] without atomics and ignores keys
-    // below the window.  The first window is a quarter octave around the row
-    // mean at 1/1024 octave per bucket: a near-flat softmax row keeps most
-    // of its keys there and spreads them over many buckets.
+    // below the window.  The first window is an eighth of an octave around
+    // the row mean at 1/2048 octave per bucket: a near-flat softmax row keeps
+    // most of its keys there, spread over many buckets, and the crossing
+    // usually falls in a bucket of <= 64 keys after this one pass.
     unsigned long long lo = 0ull, hi = kmax;
     unsigned long long whi;
     {
-      const double anchor = total / (double)Nb * 1.0905077326652577;  // 2^(1/8)
+      const double anchor = total / (double)Nb * 1.0442737824274138;  // 2^(1/16)
       const unsigned long long ka = (unsigned long long)__double_as_longlong(anchor);
       whi = ka < hi ? ka : hi;
     }
-    int s = 42;
+    int s = 41;
     int cnt_above = 0, cnt_ge_lo = Nb, band_cnt = Nb;
     double mass_above = 0.0;
     mode = 2;
     for (int pass = 0; pass < 64; ++pass) {
-      sh.hcnt[tid] = 0;
-      sh.hmass[tid] = 0.0;
-      __syncthreads();
+      // histogram hb was cleared before the previous pass's last barrier;
+      // clear the other one for the next pass
+      const int hb = pass & 1;
+      int* hcnt = sh.hcnt[hb];
+      double* hmass = sh.hmass[hb];
+      sh.hcnt[hb ^ 1][tid] = 0;
+      sh.hmass[hb ^ 1][tid] = 0.0;
       const unsigned long long top = whi >> s;
       const unsigned long long wraw = top >= 255ull ? ((top - 255ull) << s) : 0ull;
       const unsigned long long wlo = wraw > lo ? wraw : lo;
@@ -161,8 +170,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_rows(
             amass += x;
           } else {
             const int dg = 255 - (int)(top - (key[e] >> s));
-            atomicAdd(&sh.hcnt[dg], 1);
-            atomicAdd(&sh.hmass[dg], x);
+            atomicAdd(&hcnt[dg], 1);
+            atomicAdd(&hmass[dg], x);
           }
         }
       }
@@ -190,8 +199,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_rows(
         double lm = 0.0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          c4[q] = sh.hcnt[255 - 4 * lane - q];
-          m4[q] = sh.hmass[255 - 4 * lane - q];
+          c4[q] = hcnt[255 - 4 * lane - q];
+          m4[q] = hmass[255 - 4 * lane - q];
           lc += c4[q];
           lm += m4[q];
         }
@@ -226,6 +235,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_rows(
         }
         const unsigned long long bal = __ballot(hit >= 0);
         const int first = bal ? __ffsll((long long)bal) - 1 : -1;
+        if (lane == 0) sh.s_int[3] = 0;   // band gather counter
         if (c0 >= kneed && m0 >= tau + kMassMargin) {
           // the crossing lies above the window, in (whi, hi]
           if (lane == 0) {
@@ -305,8 +315,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_rows(
     }
     if (mode == 3) {
       // ------------------------------------------------ band fast path
-      if (tid == 0) sh.s_int[3] = 0;
-      __syncthreads();
+      // (the gather counter was reset by the last scan)
 #pragma unroll
       for (int e = 0; e < NPT; ++e) {
         const int j = tid + e * kThreads;
