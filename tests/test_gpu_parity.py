@@ -313,6 +313,58 @@ def test_stage4_tiny_block_counts(grid, d):
                 assert_close(g[b, h], r, True, f"{name}[{b},{h}]")
 
 
+def test_stage4_max_block_count():
+    """Nb = 8192 (the largest supported): one query block selects every KV
+    block (a union of 8192 entries), the others a few random ones; sampled
+    rows of o, lse, dq and dK / dV of little-used KV blocks against the
+    oracle."""
+    T, H, W = 32, 128, 128
+    N = T * H * W
+    nb = N // 64
+    assert nb == 8192
+    rng = np.random.default_rng(8192)
+    d = 128
+    q, k, v, do = (iid_normal((1, 1, N, d), seed=s, dtype="bf16")
+                   for s in (81, 82, 83, 84))
+    perm = _two_perms(T, H, W)[1:2]
+    counts = np.zeros((1, 1, nb), dtype=np.int32)
+    kv = np.full((1, 1, nb, nb), -1, dtype=np.int32)
+    lists = []
+    for i in range(nb):
+        L = (np.arange(nb) if i == 0 else
+             np.sort(rng.choice(nb, size=int(rng.integers(1, 17)), replace=False)))
+        counts[0, 0, i] = len(L)
+        kv[0, 0, i, :len(L)] = L
+        lists.append(L)
+    _print("max blocks", nb)
+    args = [to_dev(a) for a in (q, k, v)]
+    dperm, dcounts, dkv = to_dev(perm), to_dev(counts), to_dev(kv)
+    o, lse = P.sparse_attn_fwd(*args, dperm, dcounts, dkv)
+    dq, dk, dv = P.sparse_attn_bwd(*args, o, to_dev(do), lse, dperm, dcounts, dkv)
+    torch.cuda.synchronize()
+    o, lse = to_host(o), lse.cpu().numpy()
+    dq, dk, dv = (t.cpu().numpy() for t in (dq, dk, dv))
+    pm = perm[0]
+    q0, k0, v0, do0 = (widen(a[0, 0]) for a in (q, k, v, do))
+    blocks = [0, 1, 4095, 8191]
+    ro, rl = po.sparse_attn_fwd(q0, k0, v0, pm, lists, query_blocks=blocks)
+    rows = np.concatenate([pm[64 * i:64 * (i + 1)] for i in blocks])
+    assert_close(o[0, 0][rows], ro[rows], True, "o")
+    assert_close(lse[0, 0][rows], rl[rows], True, "lse")
+    rq, _, _ = po.sparse_attn_bwd(q0, k0, v0, do0, pm, lists, query_blocks=blocks)
+    assert_close(dq[0, 0][rows], rq[rows], True, "dq")
+    users = [[] for _ in range(nb)]
+    for i, L in enumerate(lists):
+        for j in L:
+            users[j].append(i)
+    picks = sorted(range(nb), key=lambda j: len(users[j]))[:3]
+    qb = sorted(set(i for j in picks for i in users[j]))
+    _, rk, rv = po.sparse_attn_bwd(q0, k0, v0, do0, pm, lists, query_blocks=qb)
+    cols = np.concatenate([pm[64 * j:64 * (j + 1)] for j in picks])
+    assert_close(dk[0, 0][cols], rk[cols], True, "dk")
+    assert_close(dv[0, 0][cols], rv[cols], True, "dv")
+
+
 def test_stage4_deterministic_and_poison_safe():
     c = _attn_case("bf16", 128, seed=3, B=1, Hh=2)
     args = [to_dev(c[n]) for n in ("q", "k", "v")]
