@@ -26,18 +26,6 @@
 namespace prism {
 namespace {
 
-// ------------------------------------------------------------- helpers
-template <typename E>
-__device__ __forceinline__ float ld(const E* p);
-template <>
-__device__ __forceinline__ float ld<uint16_t>(const uint16_t* p) {
-  return bf16_to_f32(*p);
-}
-template <>
-__device__ __forceinline__ float ld<float>(const float* p) {
-  return *p;
-}
-
 // D_r = <dO_r, O_r>: each thread takes one 16-byte piece of the row of O and
 // of dO (8 bf16 or 4 fp32), a group of D*sizeof(E)/16 lanes reduces a row.
 template <typename E, int D>
@@ -138,7 +126,7 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = __builtin_amdgcn_readfirstlane(wave >> 2);
   const int kh = wave & 1, qh = (wave >> 1) & 1;
-  const int c = lane & 31, hf = lane >> 5, j16 = lane & 15, grp = lane >> 4;
+  const int c = lane & 31, hf = lane >> 5;
   const long long head = bh * N;
   const int32_t* pb = perm + (long long)b * N;
   const float sl2 = scale * kLog2e;
