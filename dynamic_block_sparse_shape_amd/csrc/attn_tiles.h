@@ -3,11 +3,13 @@
 // * 64-row bf16 tiles (one 64-token block of K, V, Q or dO) live row-major in
 //   LDS with an XOR swizzle of their 16-byte pieces, so that both access
 //   patterns below are free of bank conflicts:
-//     - row-operand reads: ds_read_b128 of one 16-byte piece from 16
-//       different rows per quarter-wave;
-//     - transposed-operand reads: ds_read_b64_tr_b16 (gfx950), where each
-//       quarter-wave reads 8 bytes from 4 consecutive rows x 4 columns and
-//       the hardware hands every lane 4 consecutive rows of one column.
+//     - row-operand reads: ds_read_b128 of one 16-byte piece from each of
+//       16 rows per 16 lanes;
+//     - transposed-operand reads: ds_read_b64_tr_b16 (gfx950), where a
+//       half-wave reads 8 bytes per lane from 4 consecutive rows x 32
+//       columns and the hardware hands every lane 4 consecutive rows of one
+//       column.
+//   (The LDS bank-conflict counter reads zero for both patterns.)
 // * A workgroup (256 or 512 threads) gathers a tile's rows through the
 //   token permutation with 16-byte buffer loads held in registers one or two
 //   blocks ahead, then publishes it with one ds_write_b128 per piece.
@@ -60,9 +62,17 @@ struct Tile {
   static constexpr int kPieces = kRowBytes / 16;          // 16-byte pieces per row
   static constexpr int kBytes = 64 * kRowBytes;
 
+  // 16-byte slot of piece 0 of row r (the XOR key).  The LDS serves 256
+  // bytes (64 banks) per pass.  Row-operand reads fetch one piece from each
+  // of 16 consecutive rows: the key is a bijection on r mod 16 (D = 128;
+  // for D = 64, two rows share a pass and the key is a bijection on r / 2
+  // within each parity).  Transposed reads fetch 4 pieces (one aligned
+  // group of 4 slots) from each of 4 consecutive rows: bits 2-3 of the slot
+  // must differ between those rows, so the row's low bits go there.  The
+  // key depends on r mod 16 only.
   __device__ static __forceinline__ int swz(int r) {
-    if constexpr (kPieces == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
-    else return (r >> 1) & (kPieces - 1);
+    if constexpr (kPieces == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
   }
   // byte offset of (row r, 16-byte piece p)
   __device__ static __forceinline__ int off(int r, int p) {
