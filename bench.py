@@ -83,6 +83,9 @@ def kernel_work(name, w):
         "token_rms": ("hbm", B * N * C * esz + 8 * B * N),
         "bwd_delta": ("hbm", 2 * B * Hh * N * d * esz + 4 * B * Hh * N),
         "bitmap_build": ("hbm", 4 * sc + 4 * B * Hh * Nb),
+        "bitmap_transpose": ("hbm", 8 * B * Hh * ((Nb + 31) // 32) * Nb),
+        "pair_weights": ("hbm", 4 * B * Hh * ((Nb + 31) // 32) * Nb
+                         + 4 * 32 * B * Hh * Nb),
     }
     return table.get(name, (None, 0))
 
@@ -247,6 +250,8 @@ def main():
     dv = torch.empty_like(dq)
     wsb_bytes = P.prism_sparse_attn_bwd_workspace_bytes(B, Hh, N, d)
     wsb = torch.empty(wsb_bytes, dtype=torch.uint8, device=dev)
+    wsf = torch.empty(P.prism_sparse_attn_fwd_workspace_bytes(B, Hh, N, d),
+                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -275,7 +280,7 @@ def main():
         mark(3)
         P.prism_sparse_attn_fwd(ptr(q), ptr(k), ptr(v), dt_code, ptr(perm),
                                 ptr(counts), ptr(kv_idx), Nb, B, Hh, N, d, -1.0,
-                                ptr(o), ptr(lse), None, 0, sh)
+                                ptr(o), ptr(lse), ptr(wsf), wsf.numel(), sh)
         mark(4)
         P.prism_sparse_attn_bwd(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse),
                                 dt_code, ptr(perm), ptr(counts), ptr(kv_idx), Nb,

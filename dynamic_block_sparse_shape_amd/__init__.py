@@ -288,17 +288,22 @@ def select_blocks(proxy, top_k: int, cdf_threshold: float = 0.20,
 
 
 def sparse_attn_fwd(q, k, v, perm, counts, kv_idx,
-                    softmax_scale: Optional[float] = None, stream=None):
+                    softmax_scale: Optional[float] = None, workspace=None,
+                    stream=None):
     """Stage 4 forward.  Returns (o [B,Hh,N,d] q.dtype, lse [B,Hh,N] f32)."""
     torch = _torch()
     B, Hh, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = prism_sparse_attn_fwd_workspace_bytes(B, Hh, N, d)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     scale = -1.0 if softmax_scale is None else float(softmax_scale)
     prism_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
                           _ptr(perm), _ptr(counts), _ptr(kv_idx),
                           kv_idx.shape[-1], B, Hh, N, d, scale, _ptr(o),
-                          _ptr(lse), None, 0, _stream(stream))
+                          _ptr(lse), _ptr(workspace), workspace.numel(),
+                          _stream(stream))
     return o, lse
 
 

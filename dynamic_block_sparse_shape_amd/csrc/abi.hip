@@ -292,8 +292,8 @@ prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
 }
 
 size_t prism_sparse_attn_fwd_workspace_bytes(int B, int Hh, int N, int d) {
-  (void)B; (void)Hh; (void)N; (void)d;
-  return 0;
+  if (check_heads(B, Hh, N, d) != PRISM_OK) return 0;
+  return attn_fwd_ws_bytes(B, Hh, N, d);
 }
 
 static prism_status check_attn_common(const void* q, const void* k,
@@ -329,16 +329,23 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k,
                                    void* o, float* lse, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   clear_error();
-  (void)workspace; (void)workspace_bytes;
   prism_status st = check_attn_common(q, k, v, dtype, perm, counts, kv_idx,
                                       capacity, B, Hh, N, d, softmax_scale);
   if (st != PRISM_OK) return st;
   PRISM_CHECK(o && lse, PRISM_ERR_INVALID_ARG, "null output pointer");
   PRISM_CHECK_ALIGNED(o, 16);
   PRISM_CHECK_ALIGNED(lse, 4);
+  if (dtype == PRISM_BF16) {
+    PRISM_CHECK_ALIGNED(workspace, 16);
+    const size_t need = attn_fwd_ws_bytes(B, Hh, N, d);
+    PRISM_CHECK(workspace != nullptr && workspace_bytes >= need,
+                PRISM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                need, workspace ? workspace_bytes : (size_t)0);
+  }
   float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
   return launch_attn_fwd(q, k, v, dtype, perm, counts, kv_idx, capacity, B,
-                         Hh, N, d, scale, o, lse, (hipStream_t)stream);
+                         Hh, N, d, scale, o, lse, workspace,
+                         (hipStream_t)stream);
 }
 
 size_t prism_sparse_attn_bwd_workspace_bytes(int B, int Hh, int N, int d) {

@@ -11,10 +11,12 @@
 //   bitmap_build    word-major column bitmaps: bit i of KV block j's word
 //                   set when query block i selected j -- the KV->query
 //                   lists, read in ascending i by the dK/dV kernel.
-//   dkdv_bf16       one workgroup per pair of neighbouring KV blocks; loops
-//                   over the union of the query blocks that selected them.
-//   dq_bf16         one workgroup per pair of neighbouring query blocks;
-//                   loops over the union of their lists.
+//   pairing         pairs of KV blocks and pairs of query blocks whose
+//                   lists overlap most (pairing.hip).
+//   dkdv_bf16       one workgroup per pair of KV blocks; loops over the
+//                   union of the query blocks that selected them.
+//   dq_bf16         one workgroup per pair of query blocks; loops over the
+//                   union of their lists.
 // Both use v_mfma_f32_32x32x16_bf16 tiles with fp32 accumulation, row-major
 // swizzled LDS tiles with transposed fragments from ds_read_b64_tr_b16, and
 // register-staged gathers (see attn_tiles.h); the fp32 dtype uses plain
@@ -59,40 +61,13 @@ __global__ __launch_bounds__(256) void bwd_delta(const E* __restrict__ o,
   if (r < rows && part == 0) delta[r] = s;
 }
 
-// Column bitmaps of the selection, word-major: bits[(bh * words + w) * Nb + j]
-// holds bit i - 32 w for every query block i in [32 w, 32 w + 32) that
-// selected KV block j.  One workgroup per (bh, w) ORs its 32 lists into an
-// LDS row of Nb words and writes the row out whole (no global atomics, no
-// clearing pass).
-__global__ __launch_bounds__(256) void bitmap_build(
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ kv_idx,
-    int capacity, int Nb, int words, uint32_t* __restrict__ bits) {
-  extern __shared__ uint32_t srow[];                      // [Nb]
-  const long long bh = blockIdx.y;
-  const int w = blockIdx.x;
-  for (int j = threadIdx.x; j < Nb; j += 256) srow[j] = 0u;
-  __syncthreads();
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  for (int r = wave; r < 32; r += 4) {
-    const int i = 32 * w + r;
-    if (i >= Nb) break;
-    const long long row = bh * Nb + i;
-    const int cnt = counts[row];
-    const int32_t* lst = kv_idx + row * (long long)capacity;
-    for (int t = lane; t < cnt; t += 64) atomicOr(&srow[lst[t]], 1u << r);
-  }
-  __syncthreads();
-  uint32_t* out = bits + (bh * words + w) * (long long)Nb;
-  for (int j = threadIdx.x; j < Nb; j += 256) out[j] = srow[j];
-}
-
 // ------------------------------------------------------- dK / dV (bf16)
-// One workgroup (8 waves) per pair of neighbouring KV blocks (2p, 2p+1),
-// which are selected by largely the same query blocks.  The two column
+// One workgroup (8 waves) per pair of KV blocks (pairs[p]: neighbours in the
+// permuted order selected by largely the same query blocks).  The two column
 // bitmaps are merged into one ascending union of query blocks (entries
 // id | (selects 2p) << 13 | (selects 2p+1) << 14, 16 bits each) and each
 // query block's Q, dO, lse and D are gathered once for both.  Waves 0-3 own
-// KV block 2p and waves 4-7 block 2p+1; within a half, wave (kh, qh)
+// the pair's first KV block and waves 4-7 its second; within a half, wave (kh, qh)
 // computes KV rows 32*kh .. +31 (K, V of the block resident in LDS, B
 // operands) against query rows 32*qh .. +31.  A half skips the query blocks
 // that did not select its KV block.  Q and dO go through two LDS buffers,
@@ -105,8 +80,8 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ perm, const uint32_t* __restrict__ bits,
-    int words, int Hh, int N, long long heads, float scale,
-    float* __restrict__ dk, float* __restrict__ dv) {
+    int words, const int2* __restrict__ pairs, int Hh, int N, long long heads,
+    float scale, float* __restrict__ dk, float* __restrict__ dv) {
   using namespace tiles;
   using TL = Tile<D>;
   using SH = Share<D, 512>;
@@ -130,16 +105,17 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
   const long long head = bh * N;
   const int32_t* pb = perm + (long long)b * N;
   const float sl2 = scale * kLog2e;
-  const int j0 = 2 * pr;
-  const bool has_second = j0 + 1 < Nb;
-  const int j1 = has_second ? j0 + 1 : j0;
+  const int2 pk = pairs[bh * ((Nb + 1) / 2) + pr];
+  const int j0 = pk.x;
+  const bool has_second = pk.y >= 0;
+  const int j1 = has_second ? pk.y : j0;
 
   // ---- ascending union of the two columns (thread w owns word w)
   int ucnt = 0;
   {
     const uint32_t* col0 = bits + (bh * words + tid) * (long long)Nb + j0;
     const uint32_t wa = tid < words ? col0[0] : 0u;
-    const uint32_t wb = (tid < words && has_second) ? col0[1] : 0u;
+    const uint32_t wb = (tid < words && has_second) ? col0[j1 - j0] : 0u;
     uint32_t wu = wa | wb;
     const int n = __popc(wu);
     int incl = n;
@@ -368,9 +344,9 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
 }
 
 // ------------------------------------------------------------ dQ (bf16)
-// One workgroup (8 waves) per pair of neighbouring query blocks, as in the
-// forward: the union of the two lists is gathered once, waves 0-3 own query
-// block 2p and waves 4-7 block 2p+1, wave (qh, kh) of a half computes S^T
+// One workgroup (8 waves) per pair of query blocks, as in the forward: the
+// union of the two lists is gathered once, waves 0-3 own the pair's first
+// query block and waves 4-7 its second, wave (qh, kh) of a half computes S^T
 // and dP^T per 32x32 tile and dQ^T += K^T dS^T with K^T fragments from
 // ds_read_b64_tr_b16.  K and V go through two LDS buffers, staged two
 // blocks ahead in registers.
@@ -380,8 +356,9 @@ __global__ __launch_bounds__(512, 2) void dq_bf16(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ d_o,
     const float* __restrict__ lse, const float* __restrict__ delta,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ kv_idx, int capacity, int Hh, int N,
-    long long heads, float scale, float* __restrict__ dq) {
+    const int32_t* __restrict__ kv_idx, int capacity,
+    const int2* __restrict__ pairs, int Hh, int N, long long heads, float scale,
+    float* __restrict__ dq) {
   using namespace tiles;
   using TL = Tile<D>;
   using SH = Share<D, 512>;
@@ -404,16 +381,19 @@ __global__ __launch_bounds__(512, 2) void dq_bf16(
   const long long head = bh * N;
   const int32_t* pb = perm + (long long)b * N;
   const float sl2 = scale * kLog2e;
-  const int i0 = 2 * pr;
-  const bool has_second = i0 + 1 < Nb;
-  const long long row0 = bh * Nb + i0;
+  const int2 pq = pairs[bh * ((Nb + 1) / 2) + pr];
+  const int i0 = pq.x;
+  const bool has_second = pq.y >= 0;
+  const int i1 = has_second ? pq.y : i0;
+  const long long row0 = bh * Nb + i0, row1 = bh * Nb + i1;
   const int cnt0 = counts[row0];
-  const int cnt1 = has_second ? counts[row0 + 1] : 0;
+  const int cnt1 = has_second ? counts[row1] : 0;
   const int32_t* lst0 = kv_idx + row0 * (long long)capacity;
-  const int ucnt = pair_union(lst0, cnt0, lst0 + capacity, cnt1, Nb, bits,
-                              ulist, s_cnt, tid);
+  const int32_t* lst1 = kv_idx + row1 * (long long)capacity;
+  const int ucnt = pair_union(lst0, cnt0, lst1, cnt1, Nb, bits, ulist, s_cnt,
+                              tid);
 
-  const int iq = (half == 1 && has_second) ? i0 + 1 : i0;
+  const int iq = half == 1 ? i1 : i0;
   const int qrow = pb[64 * iq + 32 * qh + c];
   bf16x8 qreg[KS], doreg[KS];
 #pragma unroll
@@ -621,7 +601,6 @@ __global__ __launch_bounds__(64) void dkdv_f32(
   }
 }
 
-inline int bitmap_words(int Nb) { return (Nb + 31) / 32; }
 
 template <int D>
 prism_status run_bwd(const void* q, const void* k, const void* v,
@@ -631,11 +610,22 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
                      float scale, float* dq, float* dk, float* dv, void* ws,
                      hipStream_t stream) {
   const int Nb = N / 64;
-  const int words = bitmap_words(Nb);
+  const int words = (Nb + 31) / 32;
   const long long rows = (long long)B * Hh * N;
-  float* delta = static_cast<float*>(ws);
-  const size_t dbytes = ((rows * sizeof(float) + 255) / 256) * 256;
-  uint32_t* bits = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + dbytes);
+  // workspace: D rows | column bitmap | row bitmap | pairing scratch |
+  // query-block pairs | KV-block pairs
+  char* w8 = static_cast<char*>(ws);
+  float* delta = reinterpret_cast<float*>(w8);
+  w8 += align256(rows * sizeof(float));
+  uint32_t* bits = reinterpret_cast<uint32_t*>(w8);
+  w8 += bitmap_bytes(B, Hh, Nb);
+  uint32_t* rowbits = reinterpret_cast<uint32_t*>(w8);
+  w8 += bitmap_bytes(B, Hh, Nb);
+  void* pws = w8;
+  w8 += block_pairs_ws_bytes(B, Hh, Nb);
+  int2* qpairs = reinterpret_cast<int2*>(w8);
+  w8 += block_pairs_bytes(B, Hh, Nb);
+  int2* kpairs = reinterpret_cast<int2*>(w8);
 
   if (dtype == PRISM_BF16) {
     const long long rpb = 256 / (D / 8);      // rows per block
@@ -650,27 +640,33 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
   }
   prism_status st = check_launch("bwd_delta");
   if (st != PRISM_OK) return st;
-  PRISM_LAUNCH("bitmap_build", bitmap_build, dim3((unsigned)words, (unsigned)(B * Hh)),
-               dim3(256), (size_t)Nb * sizeof(uint32_t), stream, counts, kv_idx,
-               capacity, Nb, words, bits);
-  if ((st = check_launch("bitmap_build")) != PRISM_OK) return st;
+  if ((st = launch_column_bitmap(counts, kv_idx, capacity, B, Hh, Nb, bits,
+                                 stream)) != PRISM_OK)
+    return st;
 
   dim3 grid(Nb, Hh, B);
   if (dtype == PRISM_BF16) {
+    if ((st = launch_block_pairs(bits, B, Hh, Nb, pws, kpairs, stream)) != PRISM_OK)
+      return st;
+    if ((st = launch_bitmap_transpose(bits, B, Hh, Nb, rowbits, stream)) != PRISM_OK)
+      return st;
+    if ((st = launch_block_pairs(rowbits, B, Hh, Nb, pws, qpairs, stream)) != PRISM_OK)
+      return st;
     const long long heads = (long long)B * Hh;
     const dim3 gp(tiles::xcd_grid((Nb + 1) / 2, heads));
     const size_t dyn = 8 * tiles::Tile<D>::kBytes + 256 * sizeof(float) +
                        (size_t)Nb * sizeof(uint16_t);
     PRISM_LAUNCH("dkdv_bf16", dkdv_bf16<D>, gp, dim3(512), dyn, stream,
                  (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                 (const uint16_t*)d_o, lse, delta, perm, bits, words, Hh, N, heads,
-                 scale, dk, dv);
+                 (const uint16_t*)d_o, lse, delta, perm, bits, words, kpairs, Hh, N,
+                 heads, scale, dk, dv);
     if ((st = check_launch("dkdv_bf16")) != PRISM_OK) return st;
     const size_t dyn_q = 4 * tiles::Tile<D>::kBytes + 4 * (size_t)Nb +
                          8 * (size_t)((Nb + 31) / 32);
     PRISM_LAUNCH("dq_bf16", dq_bf16<D>, gp, dim3(512), dyn_q, stream, (const uint16_t*)q,
                  (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o,
-                 lse, delta, perm, counts, kv_idx, capacity, Hh, N, heads, scale, dq);
+                 lse, delta, perm, counts, kv_idx, capacity, qpairs, Hh, N, heads,
+                 scale, dq);
     return check_launch("dq_bf16");
   }
   PRISM_LAUNCH("dkdv_f32", dkdv_f32<D>, grid, dim3(64), 0, stream, (const float*)q,
@@ -688,9 +684,9 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
 size_t attn_bwd_ws_bytes(int B, int Hh, int N, int d) {
   (void)d;
   const long long rows = (long long)B * Hh * N;
-  const size_t dbytes = ((rows * sizeof(float) + 255) / 256) * 256;
   const int Nb = N / 64;
-  return dbytes + (size_t)B * Hh * Nb * bitmap_words(Nb) * sizeof(uint32_t);
+  return align256(rows * sizeof(float)) + 2 * bitmap_bytes(B, Hh, Nb) +
+         block_pairs_ws_bytes(B, Hh, Nb) + 2 * block_pairs_bytes(B, Hh, Nb);
 }
 
 prism_status launch_attn_bwd(const void* q, const void* k, const void* v,

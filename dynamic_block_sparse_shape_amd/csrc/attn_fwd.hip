@@ -19,11 +19,11 @@
 namespace prism {
 namespace {
 
-// One workgroup (8 waves) per pair of neighbouring query blocks (2p, 2p+1),
-// which select largely the same KV blocks.  The two lists are merged into
-// one ascending union in LDS; each K/V block of the union is gathered from
-// HBM once and serves both query blocks, so the gather traffic drops to the
-// union's share.  Waves 0-3 own query block 2p and waves 4-7 block 2p+1;
+// One workgroup (8 waves) per pair of query blocks (pairs[p]: neighbours in
+// the permuted order whose lists overlap most, see pairing.hip).  The two
+// lists are merged into one ascending union in LDS; each K/V block of the
+// union is gathered from HBM once and serves both query blocks, so the
+// gather traffic drops to the union's share.  Waves 0-3 own query block 2p and waves 4-7 block 2p+1;
 // within a half, wave (qh, kh) computes queries 32*qh .. +31 against KV rows
 // 32*kh .. +31 of every block, so each 32x32 MFMA tile is reused over a
 // 128-deep (S) or 32-deep (P*V) contraction.  A half skips the union blocks
@@ -36,8 +36,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ kv_idx,
-    int capacity, int Hh, int N, long long total /* B * Hh */, float scale_log2,
-    uint16_t* __restrict__ o, float* __restrict__ lse) {
+    int capacity, const int2* __restrict__ pairs, int Hh, int N,
+    long long total /* B * Hh */, float scale_log2, uint16_t* __restrict__ o,
+    float* __restrict__ lse) {
   using namespace tiles;
   using TL = Tile<D>;
   using SH = Share<D, 512>;
@@ -65,18 +66,20 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
   const int c = lane & 31, hf = lane >> 5, j16 = lane & 15, grp = lane >> 4;
   const long long head = bh * N;
   const int32_t* pb = perm + (long long)b * N;
-  const int i0 = 2 * pr;
-  const bool has_second = i0 + 1 < Nb;   // odd Nb: the last pair is a single
+  const int2 pq = pairs[bh * ((Nb + 1) / 2) + pr];
+  const int i0 = pq.x;
+  const bool has_second = pq.y >= 0;     // odd Nb: one pair is a single
+  const int i1 = has_second ? pq.y : i0;
   const long long row0 = bh * Nb + i0;
   const int cnt0 = counts[row0];
-  const int cnt1 = has_second ? counts[row0 + 1] : 0;
+  const int cnt1 = has_second ? counts[bh * Nb + i1] : 0;
   const int32_t* lst0 = kv_idx + row0 * (long long)capacity;
-  const int32_t* lst1 = lst0 + capacity;
+  const int32_t* lst1 = kv_idx + (bh * Nb + i1) * (long long)capacity;
 
   const int ucnt = pair_union(lst0, cnt0, lst1, cnt1, Nb, bits, ulist, s_cnt, tid);
 
   // a missing second block borrows the first one's rows (never written)
-  const int iq = (half == 1 && has_second) ? i0 + 1 : i0;
+  const int iq = half == 1 ? i1 : i0;
   const int qrow = pb[64 * iq + 32 * qh + c];
   bf16x8 qreg[KS];
 #pragma unroll
@@ -289,30 +292,51 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(
 
 }  // namespace
 
+size_t attn_fwd_ws_bytes(int B, int Hh, int N, int d) {
+  (void)d;
+  const int Nb = N / 64;
+  return 2 * bitmap_bytes(B, Hh, Nb) + block_pairs_ws_bytes(B, Hh, Nb) +
+         block_pairs_bytes(B, Hh, Nb);
+}
+
 prism_status launch_attn_fwd(const void* q, const void* k, const void* v,
                              int dtype, const int32_t* perm,
                              const int32_t* counts, const int32_t* kv_idx,
                              int capacity, int B, int Hh, int N, int d,
-                             float scale, void* o, float* lse,
+                             float scale, void* o, float* lse, void* ws,
                              hipStream_t stream) {
   dim3 grid(N / 64, Hh, B);
   if (dtype == PRISM_BF16) {
     const float sl2 = scale * tiles::kLog2e;
     const long long total = (long long)B * Hh;   // (batch, head) pairs
     const int Nb = N / 64;
+    // pair the query blocks: column bitmap -> row bitmap -> matching
+    char* w8 = static_cast<char*>(ws);
+    uint32_t* colbits = reinterpret_cast<uint32_t*>(w8);
+    uint32_t* rowbits = reinterpret_cast<uint32_t*>(w8 + bitmap_bytes(B, Hh, Nb));
+    void* pws = w8 + 2 * bitmap_bytes(B, Hh, Nb);
+    int2* pairs = reinterpret_cast<int2*>(static_cast<char*>(pws) +
+                                          block_pairs_ws_bytes(B, Hh, Nb));
+    prism_status st = launch_column_bitmap(counts, kv_idx, capacity, B, Hh, Nb,
+                                           colbits, stream);
+    if (st != PRISM_OK) return st;
+    if ((st = launch_bitmap_transpose(colbits, B, Hh, Nb, rowbits, stream)) != PRISM_OK)
+      return st;
+    if ((st = launch_block_pairs(rowbits, B, Hh, Nb, pws, pairs, stream)) != PRISM_OK)
+      return st;
     const dim3 g1(tiles::xcd_grid((Nb + 1) / 2, total));
     const size_t words = (size_t)(Nb + 31) / 32;
     if (d == 128) {
       const size_t dyn = 4 * tiles::Tile<128>::kBytes + 4 * (size_t)Nb + 8 * words;
       PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<128>, g1, dim3(512), dyn, stream,
                    (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                   perm, counts, kv_idx, capacity, Hh, N, total, sl2,
+                   perm, counts, kv_idx, capacity, pairs, Hh, N, total, sl2,
                    (uint16_t*)o, lse);
     } else {
       const size_t dyn = 4 * tiles::Tile<64>::kBytes + 4 * (size_t)Nb + 8 * words;
       PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<64>, g1, dim3(512), dyn, stream,
                    (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                   perm, counts, kv_idx, capacity, Hh, N, total, sl2,
+                   perm, counts, kv_idx, capacity, pairs, Hh, N, total, sl2,
                    (uint16_t*)o, lse);
     }
   } else {

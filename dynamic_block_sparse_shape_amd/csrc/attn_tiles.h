@@ -13,9 +13,10 @@
 // * A workgroup (256 or 512 threads) gathers a tile's rows through the
 //   token permutation with 16-byte buffer loads held in registers one or two
 //   blocks ahead, then publishes it with one ds_write_b128 per piece.
-// * Neighbouring blocks are processed in pairs over the union of their block
-//   lists (pair_union), and work items are ordered head by head across the 8
-//   XCDs (xcd_item).
+// * Blocks are processed in pairs over the union of their block lists
+//   (pair_union); the pairs are neighbours whose lists overlap most
+//   (pairing.hip).  Work items are ordered head by head across the 8 XCDs
+//   (xcd_item).
 // * MFMA v_mfma_f32_32x32x16_bf16 operand layouts (lane l, c = l % 32,
 //   h = l / 32): A[i][k] holds i = c, k = 8h .. 8h+7; B[k][j] holds j = c,
 //   k = 8h .. 8h+7; C[i][j] holds j = c and rows i = 8a + 4h + b in register

@@ -1,0 +1,288 @@
+// Pairing of blocks for the attention kernels.
+//
+// The forward, dQ and dK/dV kernels take two blocks per workgroup and walk
+// the union of their block lists: a tile is gathered once per union entry,
+// so the gathered bytes are proportional to |A u B| = |A| + |B| - |A n B|.
+// Pairing blocks whose lists overlap most cuts them.  Blocks are matched
+// within a window of kWin blocks on either side (permuted order: the
+// window stays inside or next to the block's zone) by the size of the
+// intersection of their lists:
+//   1. word-major bitmaps of the lists (the column bitmap of the selection
+//      is built by the backward already; the row bitmap is its bit
+//      transpose);
+//   2. weights |A n B| for every block and its 2 kWin candidates;
+//   3. rounds of mutual best choices (largest weight, ties to the lower
+//      index, weight > 0) until no pair forms, then the blocks left over in
+//      ascending order two by two.
+// The result is deterministic and every block appears in exactly one pair;
+// the attention results do not depend on it (each block still walks its own
+// list in ascending order).
+#include "prism_internal.h"
+
+namespace prism {
+namespace {
+
+constexpr int kWin = 16;          // candidates i - kWin .. i + kWin, i excluded
+constexpr int kCand = 2 * kWin;
+
+// Candidate c of block i: i - kWin + c below i, i + 1 + (c - kWin) above it
+// (ascending in the candidate's index).
+__device__ __forceinline__ int cand_of(int i, int c) {
+  return c < kWin ? i - kWin + c : i + 1 + (c - kWin);
+}
+
+// Column bitmaps of the selection, word-major: bits[(bh * words + w) * Nb + j]
+// holds bit i - 32 w for every query block i in [32 w, 32 w + 32) that
+// selected KV block j.  One workgroup per (bh, w) ORs its 32 lists (any
+// order) into an LDS row of Nb words and writes the row out whole (no
+// global atomics, no clearing pass).
+__global__ __launch_bounds__(256) void bitmap_build(
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ kv_idx,
+    int capacity, int Nb, int words, uint32_t* __restrict__ bits) {
+  extern __shared__ uint32_t srow[];                      // [Nb]
+  const long long bh = blockIdx.y;
+  const int w = blockIdx.x;
+  for (int j = threadIdx.x; j < Nb; j += 256) srow[j] = 0u;
+  __syncthreads();
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  for (int r = wave; r < 32; r += 4) {
+    const int i = 32 * w + r;
+    if (i >= Nb) break;
+    const long long row = bh * Nb + i;
+    const int cnt = counts[row];
+    const int32_t* lst = kv_idx + row * (long long)capacity;
+    for (int t = lane; t < cnt; t += 64) atomicOr(&srow[lst[t]], 1u << r);
+  }
+  __syncthreads();
+  uint32_t* out = bits + (bh * words + w) * (long long)Nb;
+  for (int j = threadIdx.x; j < Nb; j += 256) out[j] = srow[j];
+}
+
+// Bit transpose of word-major bitmaps: in[(bh * words + w) * Nb + j] holds
+// bit i - 32 w for rows i in [32 w, 32 w + 32) at column j; out[(bh * words
+// + v) * Nb + i] holds bit j - 32 v for columns j in [32 v, 32 v + 32) at
+// row i.  One wave per (bh, w, two consecutive v): each half-wave loads 32
+// words of one 32 x 32 bit tile and 32 ballots hand out its columns.
+__global__ __launch_bounds__(256) void bitmap_transpose(
+    const uint32_t* __restrict__ in, int Nb, int words, long long heads,
+    uint32_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const long long wid = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int vpairs = (words + 1) / 2;
+  const long long per_head = (long long)words * vpairs;
+  if (wid >= heads * per_head) return;        // whole wave leaves together
+  const long long bh = wid / per_head;
+  const int w = (int)(wid % per_head) / vpairs;
+  const int v = 2 * ((int)(wid % per_head) % vpairs) + (lane >> 5);
+  const int l = lane & 31;
+  const int j = 32 * v + l;
+  const uint32_t x = (v < words && j < Nb)
+                         ? in[(bh * words + w) * (long long)Nb + j] : 0u;
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int b = 0; b < 32; ++b) {
+    const unsigned long long m = __ballot((x >> b) & 1u);
+    const uint32_t half = (uint32_t)(lane < 32 ? m : m >> 32);
+    if (l == b) mine = half;
+  }
+  const int i = 32 * w + l;
+  if (v < words && i < Nb) out[(bh * words + v) * (long long)Nb + i] = mine;
+}
+
+// weight[(bh * Nb + i) * kCand + c] = |list(i) n list(cand_of(i, c))|, or -1
+// when the candidate is outside [0, Nb).  Word-major bitmap input; a
+// workgroup takes 256 consecutive blocks of one head and stages each
+// bitmap word of them and of the kWin blocks on either side in LDS.
+__global__ __launch_bounds__(256) void pair_weights(
+    const uint32_t* __restrict__ bits, int Nb, int words,
+    int32_t* __restrict__ weight) {
+  __shared__ uint32_t tile[256 + 2 * kWin];
+  const long long bh = blockIdx.y;
+  const int i0 = blockIdx.x * 256;
+  const int t = threadIdx.x;
+  const int i = i0 + t;
+  int acc[kCand];
+#pragma unroll
+  for (int c = 0; c < kCand; ++c) acc[c] = 0;
+  for (int w = 0; w < words; ++w) {
+    const uint32_t* row = bits + (bh * words + w) * (long long)Nb;
+    for (int e = t; e < 256 + 2 * kWin; e += 256) {
+      const int k = i0 - kWin + e;
+      tile[e] = (k >= 0 && k < Nb) ? row[k] : 0u;
+    }
+    __syncthreads();
+    const uint32_t a = tile[t + kWin];
+#pragma unroll
+    for (int c = 0; c < kCand; ++c)
+      acc[c] += __popc(a & tile[t + (c < kWin ? c : c + 1)]);
+    __syncthreads();
+  }
+  if (i >= Nb) return;
+  int32_t* out = weight + (bh * Nb + i) * (long long)kCand;
+#pragma unroll
+  for (int c = 0; c < kCand; ++c) {
+    const int k = cand_of(i, c);
+    out[c] = (k >= 0 && k < Nb) ? acc[c] : -1;
+  }
+}
+
+// Inclusive scan of one int per thread over a 1024-thread workgroup.
+__device__ __forceinline__ int block_scan(int x, int* s_part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  __syncthreads();
+  if (lane == 63) s_part[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += s_part[w];
+  return incl + before;
+}
+
+constexpr int kMatchThreads = 1024;
+constexpr int kMaxRounds = 64;
+
+// One workgroup per head: mutual-best rounds, then the leftovers in
+// ascending order.  pairs[bh * P + p] = (a, b), a < b or b = -1 (a single
+// block when Nb is odd), ordered by a; P = (Nb + 1) / 2.  LDS: 3 int16
+// arrays of Nb (Nb <= 8192).
+__global__ __launch_bounds__(kMatchThreads) void pair_match(
+    const int32_t* __restrict__ weight, int Nb, int2* __restrict__ pairs) {
+  extern __shared__ int16_t sm16[];
+  int16_t* partner = sm16;            // matched partner or -1
+  int16_t* best = sm16 + Nb;          // this round's choice or -1
+  int16_t* urank = sm16 + 2 * Nb;     // leftover rank -> block
+  __shared__ int s_changed, s_part[kMatchThreads / 64];
+  const long long bh = blockIdx.x;
+  const int32_t* wt = weight + bh * Nb * (long long)kCand;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < Nb; i += kMatchThreads) partner[i] = -1;
+  __syncthreads();
+  for (int round = 0; round < kMaxRounds; ++round) {
+    for (int i = tid; i < Nb; i += kMatchThreads) {
+      int bk = -1, bw = 0;
+      if (partner[i] < 0) {
+        for (int c = 0; c < kCand; ++c) {
+          const int k = cand_of(i, c);
+          const int wv = wt[(long long)i * kCand + c];
+          if (wv > bw && partner[k] < 0) {   // wv > 0 implies 0 <= k < Nb
+            bw = wv;
+            bk = k;
+          }
+        }
+      }
+      best[i] = (int16_t)bk;
+    }
+    if (tid == 0) s_changed = 0;
+    __syncthreads();
+    for (int i = tid; i < Nb; i += kMatchThreads) {
+      const int k = best[i];
+      if (k >= 0 && best[k] == i) {
+        partner[i] = (int16_t)k;
+        s_changed = 1;
+      }
+    }
+    __syncthreads();
+    const int changed = s_changed;
+    __syncthreads();
+    if (!changed) break;
+  }
+
+  // each thread owns a run of consecutive blocks [r0, r1)
+  const int per = (Nb + kMatchThreads - 1) / kMatchThreads;
+  const int r0 = min(Nb, tid * per), r1 = min(Nb, r0 + per);
+  int nu = 0;
+  for (int i = r0; i < r1; ++i) nu += partner[i] < 0;
+  const int u_incl = block_scan(nu, s_part);
+  int rank = u_incl - nu;
+  for (int i = r0; i < r1; ++i)
+    if (partner[i] < 0) urank[rank++] = (int16_t)i;
+  if (tid == kMatchThreads - 1) s_changed = u_incl;   // number of leftovers
+  __syncthreads();
+  const int nleft = s_changed;
+  // first members: matched blocks below their partner, leftovers of even
+  // rank
+  int nf = 0;
+  rank = u_incl - nu;
+  for (int i = r0; i < r1; ++i) {
+    const int pk = partner[i];
+    if (pk >= 0) nf += pk > i;
+    else nf += (rank++ & 1) == 0;
+  }
+  const int f_incl = block_scan(nf, s_part);
+  int p = f_incl - nf;
+  rank = u_incl - nu;
+  const int P = (Nb + 1) / 2;
+  int2* out = pairs + bh * P;
+  // (the first members number exactly P; the bound only guards the table)
+  for (int i = r0; i < r1; ++i) {
+    const int pk = partner[i];
+    if (pk >= 0) {
+      if (pk > i && p < P) out[p++] = int2{i, pk};
+    } else {
+      if ((rank & 1) == 0 && p < P) {
+        const int nx = rank + 1 < nleft ? urank[rank + 1] : -1;
+        out[p++] = int2{i, nx};
+      }
+      ++rank;
+    }
+  }
+}
+
+}  // namespace
+
+size_t bitmap_bytes(int B, int Hh, int Nb) {
+  return align256((size_t)B * Hh * ((Nb + 31) / 32) * Nb * sizeof(uint32_t));
+}
+
+size_t block_pairs_ws_bytes(int B, int Hh, int Nb) {
+  return align256((size_t)B * Hh * Nb * kCand * sizeof(int32_t));
+}
+
+size_t block_pairs_bytes(int B, int Hh, int Nb) {
+  return align256((size_t)B * Hh * ((Nb + 1) / 2) * sizeof(int2));
+}
+
+prism_status launch_block_pairs(const uint32_t* bits, int B, int Hh, int Nb,
+                                void* ws, int2* pairs, hipStream_t stream) {
+  const int words = (Nb + 31) / 32;
+  const long long heads = (long long)B * Hh;
+  int32_t* weight = static_cast<int32_t*>(ws);
+  PRISM_LAUNCH("pair_weights", pair_weights,
+               dim3((unsigned)((Nb + 255) / 256), (unsigned)heads), dim3(256), 0,
+               stream, bits, Nb, words, weight);
+  prism_status st = check_launch("pair_weights");
+  if (st != PRISM_OK) return st;
+  PRISM_LAUNCH("pair_match", pair_match, dim3((unsigned)heads),
+               dim3(kMatchThreads), (size_t)3 * Nb * sizeof(int16_t), stream,
+               weight, Nb, pairs);
+  return check_launch("pair_match");
+}
+
+prism_status launch_column_bitmap(const int32_t* counts, const int32_t* kv_idx,
+                                  int capacity, int B, int Hh, int Nb,
+                                  uint32_t* bits, hipStream_t stream) {
+  const int words = (Nb + 31) / 32;
+  PRISM_LAUNCH("bitmap_build", bitmap_build,
+               dim3((unsigned)words, (unsigned)(B * Hh)), dim3(256),
+               (size_t)Nb * sizeof(uint32_t), stream, counts, kv_idx, capacity,
+               Nb, words, bits);
+  return check_launch("bitmap_build");
+}
+
+prism_status launch_bitmap_transpose(const uint32_t* in, int B, int Hh, int Nb,
+                                     uint32_t* out, hipStream_t stream) {
+  const int words = (Nb + 31) / 32;
+  const long long heads = (long long)B * Hh;
+  const long long waves = heads * words * ((words + 1) / 2);
+  PRISM_LAUNCH("bitmap_transpose", bitmap_transpose,
+               dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, in, Nb,
+               words, heads, out);
+  return check_launch("bitmap_transpose");
+}
+
+}  // namespace prism

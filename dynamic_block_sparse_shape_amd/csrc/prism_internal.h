@@ -63,6 +63,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 // ------------------------------------------------------- stage launchers
 struct ZoneGeom {
@@ -85,11 +86,26 @@ prism_status launch_select(const double* proxy, int B, int Hh, int Nb,
                            int top_k, double tau, int32_t* counts,
                            int32_t* kv_idx, int capacity, hipStream_t stream);
 
+// Block pairing for the attention kernels (pairing.hip).  Bitmaps are
+// word-major: bits[(bh * words + w) * Nb + x] holds 32 bits of block x's
+// list (words = ceil(Nb / 32)).  Pairs: (Nb + 1) / 2 int2 per (b, h).
+size_t bitmap_bytes(int B, int Hh, int Nb);
+size_t block_pairs_ws_bytes(int B, int Hh, int Nb);
+size_t block_pairs_bytes(int B, int Hh, int Nb);
+prism_status launch_column_bitmap(const int32_t* counts, const int32_t* kv_idx,
+                                  int capacity, int B, int Hh, int Nb,
+                                  uint32_t* bits, hipStream_t stream);
+prism_status launch_bitmap_transpose(const uint32_t* in, int B, int Hh, int Nb,
+                                     uint32_t* out, hipStream_t stream);
+prism_status launch_block_pairs(const uint32_t* bits, int B, int Hh, int Nb,
+                                void* ws, int2* pairs, hipStream_t stream);
+
+size_t attn_fwd_ws_bytes(int B, int Hh, int N, int d);
 prism_status launch_attn_fwd(const void* q, const void* k, const void* v,
                              int dtype, const int32_t* perm,
                              const int32_t* counts, const int32_t* kv_idx,
                              int capacity, int B, int Hh, int N, int d,
-                             float scale, void* o, float* lse,
+                             float scale, void* o, float* lse, void* ws,
                              hipStream_t stream);
 
 size_t attn_bwd_ws_bytes(int B, int Hh, int N, int d);

@@ -174,12 +174,18 @@ prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
  * perm, counts, kv_idx, capacity : from stages 1 and 3.  Every count must be
  *           in [1, Nb], every listed id in [0, Nb) and the ids of one row
  *           distinct, in any order (caller's contract; stage 3 output
- *           satisfies it).  Neighbouring query blocks (2p, 2p+1) are
- *           processed together over the union of their lists.
+ *           satisfies it).  The bf16 path processes query blocks in pairs
+ *           over the union of their lists: neighbours (within 16 places in
+ *           the permuted order) whose lists overlap most, matched on the
+ *           device from the lists in every call; results do not depend on
+ *           the pairing.
  * softmax_scale : <= 0 means 1/sqrt(d).
  * o   : out [B, Hh, N, d] dtype, raster order.
  * lse : out [B, Hh, N] fp32, natural-log logsumexp of the scaled scores.
- * workspace: may be NULL (none needed; kept for future split-KV work). */
+ * workspace: bf16 -- at least prism_sparse_attn_fwd_workspace_bytes()
+ *           (list bitmaps and the pairing; about 2 * B * Hh * Nb^2 / 8
+ *           bytes); WORKSPACE if missing or smaller.  fp32 -- unused, may
+ *           be NULL. */
 size_t prism_sparse_attn_fwd_workspace_bytes(int B, int Hh, int N, int d);
 prism_status prism_sparse_attn_fwd(const void* q, const void* k,
                                    const void* v, int dtype,
@@ -199,7 +205,9 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k,
  * q, k, v, o, d_o : [B, Hh, N, d] dtype; lse [B, Hh, N] fp32 from the
  *                   forward.
  * dq, dk, dv      : out [B, Hh, N, d] fp32, raster order (fully written).
- * workspace       : at least prism_sparse_attn_bwd_workspace_bytes(). */
+ * workspace       : at least prism_sparse_attn_bwd_workspace_bytes() (D
+ *                   rows, list bitmaps, and the pairings of KV blocks and
+ *                   of query blocks, as in the forward). */
 size_t prism_sparse_attn_bwd_workspace_bytes(int B, int Hh, int N, int d);
 prism_status prism_sparse_attn_bwd(const void* q, const void* k,
                                    const void* v, const void* o,

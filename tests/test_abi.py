@@ -49,7 +49,11 @@ def test_workspace_queries():
     m = P.prism_sparse_attn_bwd_workspace_bytes(1, 24, 288000, 128)
     assert m >= 24 * 288000 * 4 + 24 * nb * ((nb + 31) // 32) * 4
     assert P.prism_sparse_attn_bwd_workspace_bytes(1, 24, 288000, 96) == 0
-    assert P.prism_sparse_attn_fwd_workspace_bytes(1, 24, 288000, 128) == 0
+    f = P.prism_sparse_attn_fwd_workspace_bytes(1, 24, 288000, 128)
+    # two list bitmaps (columns, rows) and the pairing
+    assert f >= 2 * 24 * nb * ((nb + 31) // 32) * 4 + 24 * ((nb + 1) // 2) * 8
+    assert P.prism_sparse_attn_fwd_workspace_bytes(1, 24, 288000, 96) == 0
+    assert m >= f
 
 
 def _expect(status, fn, *args, **kw):
@@ -118,6 +122,9 @@ def test_attention_rejections():
     _expect(1, P.prism_sparse_attn_fwd, *(base[:13] + [None] + base[14:]))
     _expect(1, P.prism_sparse_attn_fwd, *(base[:3] + [2] + base[4:]))
     _expect(1, P.prism_sparse_attn_fwd, *(base[:12] + [float("inf")] + base[13:]))
+    # the bf16 path needs its workspace (list bitmaps and the block pairing)
+    _expect(4, P.prism_sparse_attn_fwd, *base)
+    _expect(4, P.prism_sparse_attn_fwd, *(base[:15] + [FAKE, 16] + base[17:]))
     bwd = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 4, 1, 2,
            256, 128, -1.0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
     _expect(4, P.prism_sparse_attn_bwd, *(bwd[:20] + [8] + bwd[21:]))

@@ -374,11 +374,14 @@ def test_stage4_deterministic_and_poison_safe():
     # poison the outputs' memory, run again: everything must be rewritten
     o2 = torch.full_like(o1, float("nan"))
     l2 = torch.full_like(l1, float("nan"))
+    wsf = torch.full((P.prism_sparse_attn_fwd_workspace_bytes(1, 2, c["N"], 128),),
+                     255, dtype=torch.uint8, device="cuda")
     P.prism_sparse_attn_fwd(args[0].data_ptr(), args[1].data_ptr(),
                             args[2].data_ptr(), P.PRISM_BF16, perm.data_ptr(),
                             counts.data_ptr(), kv.data_ptr(), kv.shape[-1], 1, 2,
-                            c["N"], 128, -1.0, o2.data_ptr(), l2.data_ptr(), None,
-                            0, torch.cuda.current_stream().cuda_stream)
+                            c["N"], 128, -1.0, o2.data_ptr(), l2.data_ptr(),
+                            wsf.data_ptr(), wsf.numel(),
+                            torch.cuda.current_stream().cuda_stream)
     g2 = [torch.full_like(t, float("nan")) for t in g1]
     ws = torch.full((P.prism_sparse_attn_bwd_workspace_bytes(1, 2, c["N"], 128),),
                     255, dtype=torch.uint8, device="cuda")
