@@ -13,7 +13,13 @@
 //   2. weights |A n B| for every block and its 2 kWin candidates;
 //   3. rounds of mutual best choices (largest weight, ties to the lower
 //      index, weight > 0) until no pair forms, then the blocks left over in
-//      ascending order two by two.
+//      ascending order two by two;
+//   4. within each of the 8 ranges of the table that one XCD works through
+//      (tiles::xcd_item), the pairs are ordered by their summed list length,
+//      longest first: workgroups running side by side on an XCD then walk
+//      lists of about the same length, reach the same KV ids at about the
+//      same time and share the tiles in the XCD's L2 (and the longest work
+//      starts first).
 // The result is deterministic and every block appears in exactly one pair;
 // the attention results do not depend on it (each block still walks its own
 // list in ascending order).
@@ -90,18 +96,19 @@ __global__ __launch_bounds__(256) void bitmap_transpose(
 }
 
 // weight[(bh * Nb + i) * kCand + c] = |list(i) n list(cand_of(i, c))|, or -1
-// when the candidate is outside [0, Nb).  Word-major bitmap input; a
-// workgroup takes 256 consecutive blocks of one head and stages each
-// bitmap word of them and of the kWin blocks on either side in LDS.
+// when the candidate is outside [0, Nb); size[bh * Nb + i] = |list(i)|.
+// Word-major bitmap input; a workgroup takes 256 consecutive blocks of one
+// head and stages each bitmap word of them and of the kWin blocks on either
+// side in LDS.
 __global__ __launch_bounds__(256) void pair_weights(
     const uint32_t* __restrict__ bits, int Nb, int words,
-    int32_t* __restrict__ weight) {
+    int32_t* __restrict__ weight, int32_t* __restrict__ size) {
   __shared__ uint32_t tile[256 + 2 * kWin];
   const long long bh = blockIdx.y;
   const int i0 = blockIdx.x * 256;
   const int t = threadIdx.x;
   const int i = i0 + t;
-  int acc[kCand];
+  int acc[kCand], own = 0;
 #pragma unroll
   for (int c = 0; c < kCand; ++c) acc[c] = 0;
   for (int w = 0; w < words; ++w) {
@@ -112,12 +119,14 @@ __global__ __launch_bounds__(256) void pair_weights(
     }
     __syncthreads();
     const uint32_t a = tile[t + kWin];
+    own += __popc(a);
 #pragma unroll
     for (int c = 0; c < kCand; ++c)
       acc[c] += __popc(a & tile[t + (c < kWin ? c : c + 1)]);
     __syncthreads();
   }
   if (i >= Nb) return;
+  size[bh * Nb + i] = own;
   int32_t* out = weight + (bh * Nb + i) * (long long)kCand;
 #pragma unroll
   for (int c = 0; c < kCand; ++c) {
@@ -146,16 +155,27 @@ __device__ __forceinline__ int block_scan(int x, int* s_part) {
 constexpr int kMatchThreads = 1024;
 constexpr int kMaxRounds = 64;
 
+// LDS bytes of pair_match: 3 int16 arrays of Nb, then P pairs and P keys.
+__host__ __device__ inline size_t match_lds_bytes(int Nb) {
+  const int P = (Nb + 1) / 2;
+  return ((size_t)3 * Nb * sizeof(int16_t) + 7) / 8 * 8 +
+         (size_t)P * (sizeof(int2) + sizeof(int));
+}
+
 // One workgroup per head: mutual-best rounds, then the leftovers in
-// ascending order.  pairs[bh * P + p] = (a, b), a < b or b = -1 (a single
-// block when Nb is odd), ordered by a; P = (Nb + 1) / 2.  LDS: 3 int16
-// arrays of Nb (Nb <= 8192).
+// ascending order; then each XCD range of the table sorted by summed list
+// length, longest first (ties by first block).  pairs[bh * P + p] = (a, b),
+// a < b, or b = -1 (a single block when Nb is odd); P = (Nb + 1) / 2.
+// Nb <= 8192.
 __global__ __launch_bounds__(kMatchThreads) void pair_match(
-    const int32_t* __restrict__ weight, int Nb, int2* __restrict__ pairs) {
-  extern __shared__ int16_t sm16[];
-  int16_t* partner = sm16;            // matched partner or -1
-  int16_t* best = sm16 + Nb;          // this round's choice or -1
-  int16_t* urank = sm16 + 2 * Nb;     // leftover rank -> block
+    const int32_t* __restrict__ weight, const int32_t* __restrict__ size,
+    int Nb, int2* __restrict__ pairs) {
+  extern __shared__ __align__(8) unsigned char smb[];
+  int16_t* partner = reinterpret_cast<int16_t*>(smb);   // matched partner or -1
+  int16_t* best = partner + Nb;                         // this round's choice or -1
+  int16_t* urank = partner + 2 * Nb;                    // leftover rank -> block
+  int2* sp = reinterpret_cast<int2*>(smb + ((size_t)3 * Nb * sizeof(int16_t) + 7) / 8 * 8);
+  int* skey = reinterpret_cast<int*>(sp + (Nb + 1) / 2);
   __shared__ int s_changed, s_part[kMatchThreads / 64];
   const long long bh = blockIdx.x;
   const int32_t* wt = weight + bh * Nb * (long long)kCand;
@@ -217,19 +237,37 @@ __global__ __launch_bounds__(kMatchThreads) void pair_match(
   int p = f_incl - nf;
   rank = u_incl - nu;
   const int P = (Nb + 1) / 2;
-  int2* out = pairs + bh * P;
+  const int32_t* sz = size + bh * Nb;
   // (the first members number exactly P; the bound only guards the table)
   for (int i = r0; i < r1; ++i) {
     const int pk = partner[i];
     if (pk >= 0) {
-      if (pk > i && p < P) out[p++] = int2{i, pk};
+      if (pk > i && p < P) {
+        skey[p] = sz[i] + sz[pk];
+        sp[p++] = int2{i, pk};
+      }
     } else {
       if ((rank & 1) == 0 && p < P) {
         const int nx = rank + 1 < nleft ? urank[rank + 1] : -1;
-        out[p++] = int2{i, nx};
+        skey[p] = sz[i] + (nx >= 0 ? sz[nx] : 0);
+        sp[p++] = int2{i, nx};
       }
       ++rank;
     }
+  }
+  __syncthreads();
+  // rank within the XCD range (same split as tiles::xcd_item)
+  const int c8 = (P + 7) / 8;
+  int2* out = pairs + bh * P;
+  for (int e = tid; e < P; e += kMatchThreads) {
+    const int lo = e / c8 * c8, hi = min(P, lo + c8);
+    const int ke = skey[e];
+    int r = 0;
+    for (int f = lo; f < hi; ++f) {
+      const int kf = skey[f];
+      r += kf > ke || (kf == ke && f < e);
+    }
+    out[lo + r] = sp[e];
   }
 }
 
@@ -240,7 +278,8 @@ size_t bitmap_bytes(int B, int Hh, int Nb) {
 }
 
 size_t block_pairs_ws_bytes(int B, int Hh, int Nb) {
-  return align256((size_t)B * Hh * Nb * kCand * sizeof(int32_t));
+  return align256((size_t)B * Hh * Nb * kCand * sizeof(int32_t)) +
+         align256((size_t)B * Hh * Nb * sizeof(int32_t));
 }
 
 size_t block_pairs_bytes(int B, int Hh, int Nb) {
@@ -252,14 +291,16 @@ prism_status launch_block_pairs(const uint32_t* bits, int B, int Hh, int Nb,
   const int words = (Nb + 31) / 32;
   const long long heads = (long long)B * Hh;
   int32_t* weight = static_cast<int32_t*>(ws);
+  int32_t* size = reinterpret_cast<int32_t*>(
+      static_cast<char*>(ws) + align256((size_t)heads * Nb * kCand * sizeof(int32_t)));
   PRISM_LAUNCH("pair_weights", pair_weights,
                dim3((unsigned)((Nb + 255) / 256), (unsigned)heads), dim3(256), 0,
-               stream, bits, Nb, words, weight);
+               stream, bits, Nb, words, weight, size);
   prism_status st = check_launch("pair_weights");
   if (st != PRISM_OK) return st;
   PRISM_LAUNCH("pair_match", pair_match, dim3((unsigned)heads),
-               dim3(kMatchThreads), (size_t)3 * Nb * sizeof(int16_t), stream,
-               weight, Nb, pairs);
+               dim3(kMatchThreads), match_lds_bytes(Nb), stream, weight, size,
+               Nb, pairs);
   return check_launch("pair_match");
 }
 
