@@ -347,11 +347,13 @@ __device__ __forceinline__ int pair_union(const int32_t* __restrict__ lst0,
 }
 
 // Work item of this workgroup.  Workgroups are dealt round-robin to the 8
-// XCDs, so workgroup L runs on XCD L % 8.  Every head's Nb blocks are split
-// into 8 contiguous ranges, one per XCD, and heads are visited in order:
-// all XCDs work on the same head at the same time (one head's K / V, ~150 MB
-// at the 2K grid, is the whole working set) and each XCD's L2 sees neighbouring
-// blocks, whose block lists overlap.  Returns false for padding items.
+// XCDs, so workgroup L runs on XCD L % 8.  Every head's Nb items are split
+// into 8 contiguous ranges of the item table, one per XCD, walked in order,
+// and heads are visited in order: all XCDs work on the same head at the same
+// time (one head's K / V, ~150 MB at the 2K grid, is the whole working set).
+// The attention kernels' pair tables fill the ranges so that each XCD gets
+// an equal, longest-first share (pairing.hip).  Returns false for padding
+// items.
 __device__ __forceinline__ bool xcd_item(int Nb, long long heads, long long& bh,
                                          int& i) {
   const long long L = blockIdx.x;

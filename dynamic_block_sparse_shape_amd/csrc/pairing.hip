@@ -14,12 +14,11 @@
 //   3. rounds of mutual best choices (largest weight, ties to the lower
 //      index, weight > 0) until no pair forms, then the blocks left over in
 //      ascending order two by two;
-//   4. within each of the 8 ranges of the table that one XCD works through
-//      (tiles::xcd_item), the pairs are ordered by their summed list length,
-//      longest first: workgroups running side by side on an XCD then walk
-//      lists of about the same length, reach the same KV ids at about the
-//      same time and share the tiles in the XCD's L2 (and the longest work
-//      starts first).
+//   4. the pairs of a head are ranked by their summed list length, longest
+//      first, and dealt round-robin to the 8 ranges of the table that the 8
+//      XCDs work through (tiles::xcd_item): every XCD gets an equal share of
+//      long and short work, the longest starts first, and workgroups
+//      running side by side walk lists of about the same length.
 // The result is deterministic and every block appears in exactly one pair;
 // the attention results do not depend on it (each block still walks its own
 // list in ascending order).
@@ -163,8 +162,9 @@ __host__ __device__ inline size_t match_lds_bytes(int Nb) {
 }
 
 // One workgroup per head: mutual-best rounds, then the leftovers in
-// ascending order; then each XCD range of the table sorted by summed list
-// length, longest first (ties by first block).  pairs[bh * P + p] = (a, b),
+// ascending order; then the pairs ranked by summed list length, longest
+// first (ties by first block), rank r going to XCD range r mod 8 (ranges
+// that are full take one more).  pairs[bh * P + p] = (a, b),
 // a < b, or b = -1 (a single block when Nb is odd); P = (Nb + 1) / 2.
 // Nb <= 8192.
 __global__ __launch_bounds__(kMatchThreads) void pair_match(
@@ -256,18 +256,28 @@ __global__ __launch_bounds__(kMatchThreads) void pair_match(
     }
   }
   __syncthreads();
-  // rank within the XCD range (same split as tiles::xcd_item)
+  // global rank, dealt round-robin to the XCD ranges (same split as
+  // tiles::xcd_item: range x = [x c8, min(P, (x + 1) c8)))
   const int c8 = (P + 7) / 8;
+  const int full = P / c8, rem = P % c8;
   int2* out = pairs + bh * P;
   for (int e = tid; e < P; e += kMatchThreads) {
-    const int lo = e / c8 * c8, hi = min(P, lo + c8);
     const int ke = skey[e];
     int r = 0;
-    for (int f = lo; f < hi; ++f) {
+    for (int f = 0; f < P; ++f) {
       const int kf = skey[f];
       r += kf > ke || (kf == ke && f < e);
     }
-    out[lo + r] = sp[e];
+    int x, sidx;
+    if (r < rem * (full + 1)) {
+      sidx = r / (full + 1);
+      x = r % (full + 1);
+    } else {
+      const int r2 = r - rem * (full + 1);
+      sidx = rem + r2 / full;
+      x = r2 % full;
+    }
+    out[x * c8 + sidx] = sp[e];
   }
 }
 
