@@ -154,11 +154,18 @@ __device__ __forceinline__ int block_scan(int x, int* s_part) {
 constexpr int kMatchThreads = 1024;
 constexpr int kMaxRounds = 64;
 
-// LDS bytes of pair_match: 3 int16 arrays of Nb, then P pairs and P keys.
+// Sort keys padded to a power of two (P <= 4096).
+__host__ __device__ inline int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+// LDS bytes of pair_match: 3 int16 arrays of Nb, then P pairs and the
+// padded sort keys.
 __host__ __device__ inline size_t match_lds_bytes(int Nb) {
   const int P = (Nb + 1) / 2;
   return ((size_t)3 * Nb * sizeof(int16_t) + 7) / 8 * 8 +
-         (size_t)P * (sizeof(int2) + sizeof(int));
+         (size_t)P * sizeof(int2) + (size_t)pow2_at_least(P) * sizeof(uint32_t);
 }
 
 // One workgroup per head: mutual-best rounds, then the leftovers in
@@ -175,7 +182,7 @@ __global__ __launch_bounds__(kMatchThreads) void pair_match(
   int16_t* best = partner + Nb;                         // this round's choice or -1
   int16_t* urank = partner + 2 * Nb;                    // leftover rank -> block
   int2* sp = reinterpret_cast<int2*>(smb + ((size_t)3 * Nb * sizeof(int16_t) + 7) / 8 * 8);
-  int* skey = reinterpret_cast<int*>(sp + (Nb + 1) / 2);
+  uint32_t* skey = reinterpret_cast<uint32_t*>(sp + (Nb + 1) / 2);
   __shared__ int s_changed, s_part[kMatchThreads / 64];
   const long long bh = blockIdx.x;
   const int32_t* wt = weight + bh * Nb * (long long)kCand;
@@ -186,11 +193,22 @@ __global__ __launch_bounds__(kMatchThreads) void pair_match(
     for (int i = tid; i < Nb; i += kMatchThreads) {
       int bk = -1, bw = 0;
       if (partner[i] < 0) {
+        // the node's kCand weights: one 128-byte row, loaded as 16-byte vectors
+        int wv[kCand];
+        const int4* w4 = reinterpret_cast<const int4*>(wt + (long long)i * kCand);
+#pragma unroll
+        for (int q = 0; q < kCand / 4; ++q) {
+          const int4 x = w4[q];
+          wv[4 * q] = x.x;
+          wv[4 * q + 1] = x.y;
+          wv[4 * q + 2] = x.z;
+          wv[4 * q + 3] = x.w;
+        }
+#pragma unroll
         for (int c = 0; c < kCand; ++c) {
           const int k = cand_of(i, c);
-          const int wv = wt[(long long)i * kCand + c];
-          if (wv > bw && partner[k] < 0) {   // wv > 0 implies 0 <= k < Nb
-            bw = wv;
+          if (wv[c] > bw && partner[k] < 0) {   // weight > 0: 0 <= k < Nb
+            bw = wv[c];
             bk = k;
           }
         }
@@ -236,38 +254,56 @@ __global__ __launch_bounds__(kMatchThreads) void pair_match(
   const int f_incl = block_scan(nf, s_part);
   int p = f_incl - nf;
   rank = u_incl - nu;
-  const int P = (Nb + 1) / 2;
+  const int P = (Nb + 1) / 2, P2 = pow2_at_least(P);
   const int32_t* sz = size + bh * Nb;
+  // sort key: (32767 - summed length) << 16 | pair index -- ascending order
+  // is longest first, ties by pair index; padding sorts last
+  auto key_of = [](int len, int idx) -> uint32_t {
+    return ((uint32_t)(32767 - min(len, 32767)) << 16) | (uint32_t)idx;
+  };
   // (the first members number exactly P; the bound only guards the table)
   for (int i = r0; i < r1; ++i) {
     const int pk = partner[i];
     if (pk >= 0) {
       if (pk > i && p < P) {
-        skey[p] = sz[i] + sz[pk];
+        skey[p] = key_of(sz[i] + sz[pk], p);
         sp[p++] = int2{i, pk};
       }
     } else {
       if ((rank & 1) == 0 && p < P) {
         const int nx = rank + 1 < nleft ? urank[rank + 1] : -1;
-        skey[p] = sz[i] + (nx >= 0 ? sz[nx] : 0);
+        skey[p] = key_of(sz[i] + (nx >= 0 ? sz[nx] : 0), p);
         sp[p++] = int2{i, nx};
       }
       ++rank;
     }
   }
+  for (int e = P + tid; e < P2; e += kMatchThreads) skey[e] = 0xffffffffu;
   __syncthreads();
+  // bitonic sort of the P2 keys
+  for (int k = 2; k <= P2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int e = tid; e < P2; e += kMatchThreads) {
+        const int f = e ^ j;
+        if (f > e) {
+          const uint32_t a = skey[e], b = skey[f];
+          const bool up = (e & k) == 0;
+          if ((a > b) == up) {
+            skey[e] = b;
+            skey[f] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
   // global rank, dealt round-robin to the XCD ranges (same split as
   // tiles::xcd_item: range x = [x c8, min(P, (x + 1) c8)))
   const int c8 = (P + 7) / 8;
   const int full = P / c8, rem = P % c8;
   int2* out = pairs + bh * P;
-  for (int e = tid; e < P; e += kMatchThreads) {
-    const int ke = skey[e];
-    int r = 0;
-    for (int f = 0; f < P; ++f) {
-      const int kf = skey[f];
-      r += kf > ke || (kf == ke && f < e);
-    }
+  for (int r = tid; r < P; r += kMatchThreads) {
+    const int e = (int)(skey[r] & 0xffffu);
     int x, sidx;
     if (r < rem * (full + 1)) {
       sidx = r / (full + 1);
