@@ -316,6 +316,8 @@ static prism_status check_attn_common(const void* q, const void* k,
   PRISM_CHECK_ALIGNED(kv_idx, 4);
   PRISM_CHECK(capacity >= N / PRISM_BLOCK_TOKENS, PRISM_ERR_SHAPE,
               "capacity=%d < Nb=%d", capacity, N / PRISM_BLOCK_TOKENS);
+  PRISM_CHECK(N / PRISM_BLOCK_TOKENS <= 8192, PRISM_ERR_UNSUPPORTED,
+              "Nb=%d above 8192", N / PRISM_BLOCK_TOKENS);
   PRISM_CHECK(isfinite(softmax_scale), PRISM_ERR_INVALID_ARG,
               "softmax_scale must be finite");
   return PRISM_OK;

@@ -180,6 +180,7 @@ prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
  *           device from the lists in every call; results do not depend on
  *           the pairing.
  * softmax_scale : <= 0 means 1/sqrt(d).
+ * Nb = N / 64 must be at most 8192 (UNSUPPORTED otherwise), as in stage 2.
  * o   : out [B, Hh, N, d] dtype, raster order.
  * lse : out [B, Hh, N] fp32, natural-log logsumexp of the scaled scores.
  * workspace: bf16 -- at least prism_sparse_attn_fwd_workspace_bytes()

@@ -122,6 +122,10 @@ def test_attention_rejections():
     _expect(1, P.prism_sparse_attn_fwd, *(base[:13] + [None] + base[14:]))
     _expect(1, P.prism_sparse_attn_fwd, *(base[:3] + [2] + base[4:]))
     _expect(1, P.prism_sparse_attn_fwd, *(base[:12] + [float("inf")] + base[13:]))
+    # more than 8192 blocks per head is not supported
+    big = base[:10] + [64 * 8193] + base[11:]
+    big[7] = 8193
+    _expect(3, P.prism_sparse_attn_fwd, *big)
     # the bf16 path needs its workspace (list bitmaps and the block pairing)
     _expect(4, P.prism_sparse_attn_fwd, *base)
     _expect(4, P.prism_sparse_attn_fwd, *(base[:15] + [FAKE, 16] + base[17:]))
@@ -131,6 +135,9 @@ def test_attention_rejections():
     _expect(4, P.prism_sparse_attn_bwd, *(bwd[:19] + [None] + bwd[20:]))
     _expect(1, P.prism_sparse_attn_bwd, *(bwd[:4] + [None] + bwd[5:]))
     _expect(3, P.prism_sparse_attn_bwd, *(bwd[:14] + [32] + bwd[15:]))
+    bigb = bwd[:13] + [64 * 8193] + bwd[14:]
+    bigb[10] = 8193
+    _expect(3, P.prism_sparse_attn_bwd, *bigb)
 
 
 def test_misaligned_pointers_rejected():
