@@ -111,16 +111,29 @@ __global__ __launch_bounds__(kThreads) void zone_feat_dev(
   const int c0 = slice * CH;
   const int valid_bytes = min(CH, C - c0) * (int)sizeof(E);  // multiple of 16
 
-  // stage: 8 threads per token row, 16 bytes each
+  // stage: 8 threads per token row, 16 bytes each; every load of the thread
+  // is issued before the first LDS store, so a workgroup keeps its whole
+  // slice (up to 64 KB) in flight
+  constexpr int kIter = kMaxZoneTokens * 8 / kThreads;
   const unsigned char* fb = feat + (long long)b * N * rowB + (long long)c0 * sizeof(E);
-  for (int i = threadIdx.x; i < nt * 8; i += kThreads) {
+  uint4 v[kIter];
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int i = threadIdx.x + it * kThreads;
     const int tok = i >> 3, piece = i & 7;
-    const int lw = tok % zb.Lw, lh = (tok / zb.Lw) % zb.Lh, lt = tok / (zb.Lw * zb.Lh);
-    const long long gtok = ((long long)(zb.t0 + lt) * g.H + (zb.h0 + lh)) * g.W + zb.w0 + lw;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (piece * 16 < valid_bytes)
-      v = *reinterpret_cast<const uint4*>(fb + gtok * rowB + piece * 16);
-    *reinterpret_cast<uint4*>(tile + tok * kRowBytes + piece * 16) = v;
+    v[it] = make_uint4(0, 0, 0, 0);
+    if (tok < nt && piece * 16 < valid_bytes) {
+      const int lw = tok % zb.Lw, lh = (tok / zb.Lw) % zb.Lh, lt = tok / (zb.Lw * zb.Lh);
+      const long long gtok =
+          ((long long)(zb.t0 + lt) * g.H + (zb.h0 + lh)) * g.W + zb.w0 + lw;
+      v[it] = *reinterpret_cast<const uint4*>(fb + gtok * rowB + piece * 16);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kIter; ++it) {
+    const int i = threadIdx.x + it * kThreads;
+    if ((i >> 3) < nt)
+      *reinterpret_cast<uint4*>(tile + (i >> 3) * kRowBytes + (i & 7) * 16) = v[it];
   }
   __syncthreads();
 
