@@ -65,10 +65,10 @@ __global__ __launch_bounds__(256) void bwd_delta(const E* __restrict__ o,
 // One workgroup (8 waves) per pair of KV blocks (pairs[p]: neighbours in the
 // permuted order selected by largely the same query blocks).  The two column
 // bitmaps are merged into one ascending union of query blocks (entries
-// id | (selects 2p) << 13 | (selects 2p+1) << 14, 16 bits each) and each
-// query block's Q, dO, lse and D are gathered once for both.  Waves 0-3 own
-// the pair's first KV block and waves 4-7 its second; within a half, wave (kh, qh)
-// computes KV rows 32*kh .. +31 (K, V of the block resident in LDS, B
+// id | (selects the first) << 13 | (selects the second) << 14, 16 bits
+// each) and each query block's Q, dO, lse and D are gathered once for both.
+// Waves 0-3 own the pair's first KV block and waves 4-7 its second; within
+// a half, wave (kh, qh) computes KV rows 32*kh .. +31 (K, V of the block resident in LDS, B
 // operands) against query rows 32*qh .. +31.  A half skips the query blocks
 // that did not select its KV block.  Q and dO go through two LDS buffers,
 // staged one block ahead in registers; Q^T / dO^T fragments come from

@@ -23,8 +23,8 @@ namespace {
 // the permuted order whose lists overlap most, see pairing.hip).  The two
 // lists are merged into one ascending union in LDS; each K/V block of the
 // union is gathered from HBM once and serves both query blocks, so the
-// gather traffic drops to the union's share.  Waves 0-3 own query block 2p and waves 4-7 block 2p+1;
-// within a half, wave (qh, kh) computes queries 32*qh .. +31 against KV rows
+// gather traffic drops to the union's share.  Waves 0-3 own the pair's
+// first query block and waves 4-7 its second; within a half, wave (qh, kh) computes queries 32*qh .. +31 against KV rows
 // 32*kh .. +31 of every block, so each 32x32 MFMA tile is reused over a
 // 128-deep (S) or 32-deep (P*V) contraction.  A half skips the union blocks
 // its own list does not hold.  The two kh waves of a query half keep
