@@ -170,10 +170,11 @@ __host__ __device__ inline size_t match_lds_bytes(int Nb) {
 
 // One workgroup per head: mutual-best rounds, then the leftovers in
 // ascending order; then the pairs ranked by summed list length, longest
-// first (ties by first block), rank r going to XCD range r mod 8 (ranges
-// that are full take one more).  pairs[bh * P + p] = (a, b),
-// a < b, or b = -1 (a single block when Nb is odd); P = (Nb + 1) / 2.
-// Nb <= 8192.
+// first (ties by first block), and dealt to the XCD ranges like cards:
+// rank r to range r mod 8, position r / 8, skipping ranges that are
+// already full (the last ranges are shorter when P is not a multiple of
+// their length).  pairs[bh * P + p] = (a, b), a < b, or b = -1 (a single
+// block when Nb is odd); P = (Nb + 1) / 2.  Nb <= 8192.
 __global__ __launch_bounds__(kMatchThreads) void pair_match(
     const int32_t* __restrict__ weight, const int32_t* __restrict__ size,
     int Nb, int2* __restrict__ pairs) {
