@@ -365,6 +365,35 @@ def test_stage4_max_block_count():
     assert_close(dv[0, 0][cols], rv[cols], True, "dv")
 
 
+def test_stage4_list_order_does_not_matter():
+    """The ABI takes each row's ids in any order: the bf16 kernels walk the
+    ascending union of a pair's lists, so shuffled lists must give
+    bit-identical outputs and gradients."""
+    c = _attn_case("bf16", 128, seed=5, B=2, Hh=2)
+    _print("list order")
+    args = [to_dev(c[n]) for n in ("q", "k", "v")]
+    perm, counts = to_dev(c["perm"]), to_dev(c["counts"])
+    kv = c["kv"]
+    rng = np.random.default_rng(77)
+    shuffled = kv.copy()
+    for b in range(c["B"]):
+        for h in range(c["Hh"]):
+            for i in range(kv.shape[2]):
+                n = int(c["counts"][b, h, i])
+                shuffled[b, h, i, :n] = rng.permutation(kv[b, h, i, :n])
+    assert not np.array_equal(shuffled, kv)
+    do = to_dev(c["do"])
+    outs = []
+    for lists in (kv, shuffled):
+        kvd = to_dev(lists)
+        o, lse = P.sparse_attn_fwd(*args, perm, counts, kvd)
+        g = P.sparse_attn_bwd(*args, o, do, lse, perm, counts, kvd)
+        torch.cuda.synchronize()
+        outs.append([o, lse, *g])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 def test_stage4_deterministic_and_poison_safe():
     c = _attn_case("bf16", 128, seed=3, B=1, Hh=2)
     args = [to_dev(c[n]) for n in ("q", "k", "v")]
