@@ -90,6 +90,16 @@ def kernel_work(name, w):
     return table.get(name, (None, 0))
 
 
+def counts_histogram(counts, Nb, bins=10):
+    """Histogram of the per-row block counts c_i (1 <= c_i <= Nb): `bins`
+    equal-width bins over [1, max c_i], as {"edges": [...], "rows": [...]}."""
+    import numpy as np
+    top = int(min(Nb, counts.max()))
+    edges = np.linspace(1, top + 1, bins + 1)
+    rows, _ = np.histogram(counts.reshape(-1), bins=edges)
+    return {"edges": [int(round(e)) for e in edges], "rows": [int(r) for r in rows]}
+
+
 def source_sha(kernel_file):
     with open(os.path.join(ROOT, "dynamic_block_sparse_shape_amd", "csrc",
                            kernel_file), "rb") as f:
@@ -397,6 +407,7 @@ def main():
         "sigma_c": sigma_c,
         "counts_mean": float(counts_host.mean()),
         "counts_max": int(counts_host.max()),
+        "counts_hist": counts_histogram(counts_host, Nb),
         "stage_ms": stage_ms,
         "kernels": kernels,
     }
