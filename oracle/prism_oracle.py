@@ -421,6 +421,86 @@ def sparse_attn_bwd(q, k, v, do, perm, lists, scale: Optional[float] = None,
 
 
 # ---------------------------------------------------------------------------
+# Stage 4 variant: pooled stand-in for the unselected blocks (reading R21)
+# ---------------------------------------------------------------------------
+def dropped_block_terms(q_mean, k_mean, v_mean, lists):
+    """Weight and mean value of the blocks each query block left out (R21).
+
+    Sol-Attn abstract page: instead of discarding unselected blocks, their
+    proxy scores are reused to approximate what they contribute, inside the
+    same online softmax.  Reading: an unselected KV block j counts, for every
+    query row of block i, as its 64 keys all scoring the pooled logit
+    z_ij = <qbar_i, kbar_j> / sqrt(d) (stage 2's logit) and all carrying the
+    block's mean value vbar_j.
+
+    Returns (drop_lse [nb], drop_v [nb, dv]): drop_lse_i is the natural log
+    of sum over unselected j of 64 exp(z_ij) (-inf when block i selected
+    every block) and drop_v_i the mean of vbar_j under those weights (zero
+    then).
+    """
+    q_mean = np.asarray(q_mean, dtype=np.float64)
+    k_mean = np.asarray(k_mean, dtype=np.float64)
+    v_mean = np.asarray(v_mean, dtype=np.float64)
+    d = q_mean.shape[1]
+    z = (q_mean @ k_mean.T) / math.sqrt(d)
+    nq, nb = z.shape
+    drop_lse = np.full(nq, -np.inf)
+    drop_v = np.zeros((nq, v_mean.shape[1]))
+    for i in range(nq):
+        out = np.ones(nb, dtype=bool)
+        out[np.asarray(lists[i], dtype=np.int64)] = False
+        if not out.any():
+            continue
+        zi = z[i, out] + math.log(BLOCK)        # 64 keys per block
+        m = zi.max()
+        w = np.exp(zi - m)
+        drop_lse[i] = m + math.log(w.sum())
+        drop_v[i] = (w / w.sum()) @ v_mean[out]
+    return drop_lse, drop_v
+
+
+def sparse_attn_fwd_corrected(q, k, v, perm, lists,
+                              scale: Optional[float] = None,
+                              query_blocks: Optional[Sequence[int]] = None):
+    """Block-sparse attention plus the pooled stand-in of unselected blocks.
+
+    Reading R21 written out: query row r of block i attends to the selected
+    blocks' keys with their exact scores q_r . k_c * scale, and to 64 copies
+    of (logit z_ij, value vbar_j) for every block j it did not select, where
+    z_ij = <qbar_i, kbar_j> / sqrt(d) and the bars are block means (stage 2).
+    One softmax over both sets.  Same layout and ``query_blocks`` behaviour
+    as ``sparse_attn_fwd``; with every block selected the two are equal.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nb = N // BLOCK
+    qm, km, vm = (pool_blocks(x, perm) for x in (q, k, v))
+    z = (qm @ km.T) / math.sqrt(d)
+    o = np.full((N, v.shape[1]), np.nan)
+    lse = np.full(N, np.nan)
+    blocks = range(nb) if query_blocks is None else query_blocks
+    for i in blocks:
+        rows = _block_rows(perm, i)
+        sel = np.asarray(lists[i], dtype=np.int64)
+        out = np.setdiff1d(np.arange(nb), sel)
+        cols = _kv_rows(perm, sel)
+        s = (q[rows] @ k[cols].T) * scale
+        zd = np.repeat(z[i, out], BLOCK)                # 64 keys per block
+        logits = np.concatenate([s, np.broadcast_to(zd, (BLOCK, zd.size))],
+                                axis=1)
+        vals = np.concatenate([v[cols], np.repeat(vm[out], BLOCK, axis=0)])
+        m = logits.max(axis=1, keepdims=True)
+        l = np.log(np.exp(logits - m).sum(axis=1, keepdims=True)) + m
+        o[rows] = np.exp(logits - l) @ vals
+        lse[rows] = l[:, 0]
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
 # Whole path for one (batch, head)
 # ---------------------------------------------------------------------------
 def route_head(q, k, perm, top_k, cdf_threshold):
