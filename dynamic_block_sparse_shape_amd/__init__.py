@@ -4,12 +4,15 @@ block-sparse video self-attention library.
 The five C entry points are exposed under their C names with the C argument
 order (device pointers as ints, ``stream`` as a hipStream_t handle):
 ``prism_zone_shapes``, ``prism_pool_blocks``, ``prism_select_blocks``,
-``prism_sparse_attn_fwd``, ``prism_sparse_attn_bwd``.  This module only
+``prism_sparse_attn_fwd``, ``prism_sparse_attn_bwd``; so are the two calls of
+the forward-only variant that keeps a pooled stand-in of the unselected
+blocks, ``prism_dropped_terms`` and ``prism_sparse_attn_fwd_corrected``.  This module only
 marshals arguments; every step runs in the library's HIP kernels.  There is
 no fallback: if the library is missing, loading fails with an error.
 
 Torch-tensor helpers (``zone_shapes``, ``pool_blocks``, ``select_blocks``,
-``sparse_attn_fwd``, ``sparse_attn_bwd``) allocate outputs with torch on the
+``sparse_attn_fwd``, ``sparse_attn_bwd``, ``dropped_terms``,
+``sparse_attn_fwd_corrected``) allocate outputs with torch on the
 current device and pass the current stream.
 """
 from __future__ import annotations
@@ -24,11 +27,14 @@ __all__ = [
     "prism_sparse_attn_fwd", "prism_sparse_attn_bwd",
     "prism_zone_shapes_workspace_bytes", "prism_sparse_attn_bwd_workspace_bytes",
     "prism_sparse_attn_fwd_workspace_bytes", "prism_shape_table",
+    "prism_dropped_terms", "prism_dropped_terms_workspace_bytes",
+    "prism_sparse_attn_fwd_corrected",
     "prism_last_error", "prism_version", "prism_profile_enable",
     "prism_profile_reset", "prism_profile_count", "prism_profile_name",
     "prism_profile_ms", "kernel_times",
     "zone_shapes", "pool_blocks", "select_blocks", "sparse_attn_fwd",
-    "sparse_attn_bwd", "shape_table",
+    "sparse_attn_bwd", "shape_table", "dropped_terms",
+    "sparse_attn_fwd_corrected",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libprism.so")
@@ -64,6 +70,16 @@ _SIGS = {
                                        _c_p, _c_int, _c_int, _c_int, _c_int,
                                        _c_int, _c_flt, _c_p, _c_p, _c_p, _c_sz,
                                        _c_p]),
+    "prism_dropped_terms_workspace_bytes": (_c_sz, [_c_int] * 4),
+    "prism_dropped_terms": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_int, _c_p,
+                                     _c_p, _c_p, _c_int, _c_int, _c_int,
+                                     _c_int, _c_int, _c_p, _c_p, _c_p, _c_sz,
+                                     _c_p]),
+    "prism_sparse_attn_fwd_corrected": (_c_int, [_c_p, _c_p, _c_p, _c_int, _c_p,
+                                                 _c_p, _c_p, _c_int, _c_int,
+                                                 _c_int, _c_int, _c_int, _c_flt,
+                                                 _c_p, _c_p, _c_p, _c_p, _c_p,
+                                                 _c_sz, _c_p]),
     "prism_sparse_attn_bwd_workspace_bytes": (_c_sz, [_c_int] * 4),
     "prism_sparse_attn_bwd": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                        _c_int, _c_p, _c_p, _c_p, _c_int,
@@ -181,6 +197,27 @@ def prism_sparse_attn_fwd(q, k, v, dtype, perm, counts, kv_idx, capacity, B,
     return _call("prism_sparse_attn_fwd", q, k, v, dtype, perm, counts,
                  kv_idx, capacity, B, Hh, N, d, softmax_scale, o, lse,
                  workspace, workspace_bytes, stream)
+
+
+def prism_dropped_terms_workspace_bytes(B, Hh, N, d) -> int:
+    return lib().prism_dropped_terms_workspace_bytes(B, Hh, N, d)
+
+
+def prism_dropped_terms(proxy, q_mean, k_mean, v, dtype, perm, counts, kv_idx,
+                        capacity, B, Hh, N, d, drop_lse, drop_v, workspace,
+                        workspace_bytes, stream):
+    return _call("prism_dropped_terms", proxy, q_mean, k_mean, v, dtype, perm,
+                 counts, kv_idx, capacity, B, Hh, N, d, drop_lse, drop_v,
+                 workspace, workspace_bytes, stream)
+
+
+def prism_sparse_attn_fwd_corrected(q, k, v, dtype, perm, counts, kv_idx,
+                                    capacity, B, Hh, N, d, softmax_scale,
+                                    drop_lse, drop_v, o, lse, workspace,
+                                    workspace_bytes, stream):
+    return _call("prism_sparse_attn_fwd_corrected", q, k, v, dtype, perm,
+                 counts, kv_idx, capacity, B, Hh, N, d, softmax_scale,
+                 drop_lse, drop_v, o, lse, workspace, workspace_bytes, stream)
 
 
 def prism_sparse_attn_bwd(q, k, v, o, d_o, lse, dtype, perm, counts, kv_idx,
@@ -326,3 +363,45 @@ def sparse_attn_bwd(q, k, v, o, d_o, lse, perm, counts, kv_idx,
                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                           workspace.numel(), _stream(stream))
     return dq, dk, dv
+
+
+def dropped_terms(proxy, q_mean, k_mean, v, perm, counts, kv_idx,
+                  workspace=None, stream=None):
+    """Stand-in of the unselected blocks (forward-only variant).  Returns
+    (drop_lse [B,Hh,Nb] f32, drop_v [B,Hh,Nb,d] f32)."""
+    torch = _torch()
+    B, Hh, N, d = v.shape
+    Nb = N // 64
+    drop_lse = torch.empty((B, Hh, Nb), dtype=torch.float32, device=v.device)
+    drop_v = torch.empty((B, Hh, Nb, d), dtype=torch.float32, device=v.device)
+    if workspace is None:
+        need = prism_dropped_terms_workspace_bytes(B, Hh, N, d)
+        workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+    prism_dropped_terms(_ptr(proxy), _ptr(q_mean), _ptr(k_mean), _ptr(v),
+                        _dtype_code(v), _ptr(perm), _ptr(counts), _ptr(kv_idx),
+                        kv_idx.shape[-1], B, Hh, N, d, _ptr(drop_lse),
+                        _ptr(drop_v), _ptr(workspace), workspace.numel(),
+                        _stream(stream))
+    return drop_lse, drop_v
+
+
+def sparse_attn_fwd_corrected(q, k, v, perm, counts, kv_idx, drop_lse, drop_v,
+                              softmax_scale: Optional[float] = None,
+                              workspace=None, stream=None):
+    """Stage 4 forward with the stand-in of the unselected blocks in the same
+    softmax.  Returns (o [B,Hh,N,d] q.dtype, lse [B,Hh,N] f32)."""
+    torch = _torch()
+    B, Hh, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hh, N), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = prism_sparse_attn_fwd_workspace_bytes(B, Hh, N, d)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    scale = -1.0 if softmax_scale is None else float(softmax_scale)
+    prism_sparse_attn_fwd_corrected(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q),
+                                    _ptr(perm), _ptr(counts), _ptr(kv_idx),
+                                    kv_idx.shape[-1], B, Hh, N, d, scale,
+                                    _ptr(drop_lse), _ptr(drop_v), _ptr(o),
+                                    _ptr(lse), _ptr(workspace),
+                                    workspace.numel(), _stream(stream))
+    return o, lse

@@ -346,7 +346,79 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k,
   }
   float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
   return launch_attn_fwd(q, k, v, dtype, perm, counts, kv_idx, capacity, B,
-                         Hh, N, d, scale, o, lse, workspace,
+                         Hh, N, d, scale, nullptr, nullptr, o, lse, workspace,
+                         (hipStream_t)stream);
+}
+
+size_t prism_dropped_terms_workspace_bytes(int B, int Hh, int N, int d) {
+  if (check_heads(B, Hh, N, d) != PRISM_OK) return 0;
+  return dropped_terms_ws_bytes(B, Hh, N, d);
+}
+
+prism_status prism_dropped_terms(const double* proxy, const double* q_mean,
+                                 const double* k_mean, const void* v,
+                                 int dtype, const int32_t* perm,
+                                 const int32_t* counts, const int32_t* kv_idx,
+                                 int capacity, int B, int Hh, int N, int d,
+                                 float* drop_lse, float* drop_v,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  clear_error();
+  prism_status st = check_heads(B, Hh, N, d);
+  if (st != PRISM_OK) return st;
+  PRISM_CHECK(dtype_ok(dtype), PRISM_ERR_INVALID_ARG, "bad dtype %d", dtype);
+  PRISM_CHECK(proxy && q_mean && k_mean && v && perm && counts && kv_idx &&
+                  drop_lse && drop_v,
+              PRISM_ERR_INVALID_ARG, "null pointer argument");
+  PRISM_CHECK_ALIGNED(proxy, 8);
+  PRISM_CHECK_ALIGNED(q_mean, 8);
+  PRISM_CHECK_ALIGNED(k_mean, 8);
+  PRISM_CHECK_ALIGNED(v, 16);
+  PRISM_CHECK_ALIGNED(perm, 4);
+  PRISM_CHECK_ALIGNED(counts, 4);
+  PRISM_CHECK_ALIGNED(kv_idx, 4);
+  PRISM_CHECK_ALIGNED(drop_lse, 4);
+  PRISM_CHECK_ALIGNED(drop_v, 16);
+  PRISM_CHECK_ALIGNED(workspace, 16);
+  const int Nb = N / PRISM_BLOCK_TOKENS;
+  PRISM_CHECK(capacity >= Nb, PRISM_ERR_SHAPE, "capacity=%d < Nb=%d", capacity,
+              Nb);
+  PRISM_CHECK(Nb <= 8192, PRISM_ERR_UNSUPPORTED, "Nb=%d above 8192", Nb);
+  const size_t need = dropped_terms_ws_bytes(B, Hh, N, d);
+  PRISM_CHECK(workspace != nullptr && workspace_bytes >= need,
+              PRISM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+              need, workspace ? workspace_bytes : (size_t)0);
+  return launch_dropped_terms(proxy, q_mean, k_mean, v, dtype, perm, counts,
+                              kv_idx, capacity, B, Hh, N, d, drop_lse, drop_v,
+                              workspace, (hipStream_t)stream);
+}
+
+prism_status prism_sparse_attn_fwd_corrected(
+    const void* q, const void* k, const void* v, int dtype,
+    const int32_t* perm, const int32_t* counts, const int32_t* kv_idx,
+    int capacity, int B, int Hh, int N, int d, float softmax_scale,
+    const float* drop_lse, const float* drop_v, void* o, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  prism_status st = check_attn_common(q, k, v, dtype, perm, counts, kv_idx,
+                                      capacity, B, Hh, N, d, softmax_scale);
+  if (st != PRISM_OK) return st;
+  PRISM_CHECK(o && lse && drop_lse && drop_v, PRISM_ERR_INVALID_ARG,
+              "null pointer argument");
+  PRISM_CHECK_ALIGNED(o, 16);
+  PRISM_CHECK_ALIGNED(lse, 4);
+  PRISM_CHECK_ALIGNED(drop_lse, 4);
+  PRISM_CHECK_ALIGNED(drop_v, 16);
+  if (dtype == PRISM_BF16) {
+    PRISM_CHECK_ALIGNED(workspace, 16);
+    const size_t need = attn_fwd_ws_bytes(B, Hh, N, d);
+    PRISM_CHECK(workspace != nullptr && workspace_bytes >= need,
+                PRISM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                need, workspace ? workspace_bytes : (size_t)0);
+  }
+  float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+  return launch_attn_fwd(q, k, v, dtype, perm, counts, kv_idx, capacity, B,
+                         Hh, N, d, scale, drop_lse, drop_v, o, lse, workspace,
                          (hipStream_t)stream);
 }
 

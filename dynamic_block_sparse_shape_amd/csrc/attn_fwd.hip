@@ -37,8 +37,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
     const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ kv_idx,
     int capacity, const int2* __restrict__ pairs, int Hh, int N,
-    long long total /* B * Hh */, float scale_log2, uint16_t* __restrict__ o,
-    float* __restrict__ lse) {
+    long long total /* B * Hh */, float scale_log2,
+    const float* __restrict__ drop_lse, const float* __restrict__ drop_v,
+    uint16_t* __restrict__ o, float* __restrict__ lse) {
   using namespace tiles;
   using TL = Tile<D>;
   using SH = Share<D, 512>;
@@ -219,9 +220,23 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
   __syncthreads();
   if (kh == 0 && (half == 0 || has_second)) {
     const float m2 = sm_m[half][qh][c], l2 = sm_l[half][qh][c];
-    const float m = fmaxf(m_run, m2);
+    float m = fmaxf(m_run, m2);
     const float a1 = exp2_fast(m_run - m), a2 = exp2_fast(m2 - m);
-    const float l = l_run * a1 + l2 * a2;
+    float l = l_run * a1 + l2 * a2;
+    // optional stand-in of the blocks this query block did not keep: weight
+    // exp(drop_lse) (natural log) with value drop_v, one more term of the
+    // same softmax
+    float b1 = 1.f, b2 = 0.f;
+    const float* dvr = nullptr;
+    if (drop_lse != nullptr) {
+      const float dl = drop_lse[bh * Nb + iq] * kLog2e;
+      const float mm = fmaxf(m, dl);
+      b1 = exp2_fast(m - mm);
+      b2 = exp2_fast(dl - mm);
+      m = mm;
+      l = l * b1 + b2;
+      dvr = drop_v + (bh * Nb + iq) * D;
+    }
     const float inv_l = 1.f / l;
     uint16_t* orow = o + (head + qrow) * D;
 #pragma unroll
@@ -232,8 +247,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int r = 4 * a + bb;
-          vals[bb] = (oacc[mt][r] * a1 +
-                      xo[((qh * 64 + lane) * DT + mt) * 16 + r] * a2) * inv_l;
+          const float x = oacc[mt][r] * a1 +
+                          xo[((qh * 64 + lane) * DT + mt) * 16 + r] * a2;
+          vals[bb] = dvr ? (x * b1 + b2 * dvr[32 * mt + 8 * a + 4 * hf + bb]) * inv_l
+                         : x * inv_l;
         }
         uint2 pk;
         pk.x = cvt2(vals[0], vals[1]);
@@ -250,8 +267,9 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(
     const float* __restrict__ q, const float* __restrict__ k,
     const float* __restrict__ v, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ kv_idx,
-    int capacity, int Hh, int N, float scale, float* __restrict__ o,
-    float* __restrict__ lse) {
+    int capacity, int Hh, int N, float scale,
+    const float* __restrict__ drop_lse, const float* __restrict__ drop_v,
+    float* __restrict__ o, float* __restrict__ lse) {
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int Nb = N / 64;
   const long long head = ((long long)b * Hh + h) * N;
@@ -284,6 +302,20 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(
       m_run = m_new;
     }
   }
+  if (drop_lse != nullptr) {
+    // stand-in of the blocks this query block did not keep
+    const float dl = drop_lse[rowid];
+    const float mm = fmaxf(m_run, dl);
+    const float b1 = expf(m_run - mm), b2 = expf(dl - mm);
+    const float l = l_run * b1 + b2;
+    const float* dvr = drop_v + rowid * D;
+    const float inv_l = 1.f / l;
+#pragma unroll
+    for (int e = 0; e < D; ++e)
+      o[(head + qrow) * D + e] = (acc[e] * b1 + b2 * dvr[e]) * inv_l;
+    lse[head + qrow] = mm + logf(l);
+    return;
+  }
   const float inv_l = 1.f / l_run;
 #pragma unroll
   for (int e = 0; e < D; ++e) o[(head + qrow) * D + e] = acc[e] * inv_l;
@@ -303,8 +335,9 @@ prism_status launch_attn_fwd(const void* q, const void* k, const void* v,
                              int dtype, const int32_t* perm,
                              const int32_t* counts, const int32_t* kv_idx,
                              int capacity, int B, int Hh, int N, int d,
-                             float scale, void* o, float* lse, void* ws,
-                             hipStream_t stream) {
+                             float scale, const float* drop_lse,
+                             const float* drop_v, void* o, float* lse,
+                             void* ws, hipStream_t stream) {
   dim3 grid(N / 64, Hh, B);
   if (dtype == PRISM_BF16) {
     const float sl2 = scale * tiles::kLog2e;
@@ -331,23 +364,25 @@ prism_status launch_attn_fwd(const void* q, const void* k, const void* v,
       PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<128>, g1, dim3(512), dyn, stream,
                    (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                    perm, counts, kv_idx, capacity, pairs, Hh, N, total, sl2,
-                   (uint16_t*)o, lse);
+                   drop_lse, drop_v, (uint16_t*)o, lse);
     } else {
       const size_t dyn = 4 * tiles::Tile<64>::kBytes + 4 * (size_t)Nb + 8 * words;
       PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<64>, g1, dim3(512), dyn, stream,
                    (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                    perm, counts, kv_idx, capacity, pairs, Hh, N, total, sl2,
-                   (uint16_t*)o, lse);
+                   drop_lse, drop_v, (uint16_t*)o, lse);
     }
   } else {
     if (d == 128)
       PRISM_LAUNCH("attn_fwd_f32", attn_fwd_f32<128>, grid, dim3(64), 0, stream,
                          (const float*)q, (const float*)k, (const float*)v, perm,
-                         counts, kv_idx, capacity, Hh, N, scale, (float*)o, lse);
+                         counts, kv_idx, capacity, Hh, N, scale, drop_lse, drop_v,
+                         (float*)o, lse);
     else
       PRISM_LAUNCH("attn_fwd_f32", attn_fwd_f32<64>, grid, dim3(64), 0, stream,
                          (const float*)q, (const float*)k, (const float*)v, perm,
-                         counts, kv_idx, capacity, Hh, N, scale, (float*)o, lse);
+                         counts, kv_idx, capacity, Hh, N, scale, drop_lse, drop_v,
+                         (float*)o, lse);
   }
   return check_launch("attn_fwd");
 }

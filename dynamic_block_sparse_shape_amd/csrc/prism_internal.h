@@ -105,8 +105,20 @@ prism_status launch_attn_fwd(const void* q, const void* k, const void* v,
                              int dtype, const int32_t* perm,
                              const int32_t* counts, const int32_t* kv_idx,
                              int capacity, int B, int Hh, int N, int d,
-                             float scale, void* o, float* lse, void* ws,
-                             hipStream_t stream);
+                             float scale, const float* drop_lse,
+                             const float* drop_v, void* o, float* lse,
+                             void* ws, hipStream_t stream);
+
+// Pooled stand-in for the unselected blocks (dropped.hip): per query block
+// the log weight drop_lse [B,Hh,Nb] and mean value drop_v [B,Hh,Nb,d] (fp32).
+size_t dropped_terms_ws_bytes(int B, int Hh, int N, int d);
+prism_status launch_dropped_terms(const double* proxy, const double* q_mean,
+                                  const double* k_mean, const void* v,
+                                  int dtype, const int32_t* perm,
+                                  const int32_t* counts, const int32_t* kv_idx,
+                                  int capacity, int B, int Hh, int N, int d,
+                                  float* drop_lse, float* drop_v, void* ws,
+                                  hipStream_t stream);
 
 size_t attn_bwd_ws_bytes(int B, int Hh, int N, int d);
 prism_status launch_attn_bwd(const void* q, const void* k, const void* v,

@@ -221,6 +221,56 @@ prism_status prism_sparse_attn_bwd(const void* q, const void* k,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);
 
+/* ---------------------------------------------------------------------
+ * Stage 4 variant (forward only) -- a pooled stand-in for the KV blocks a
+ * query block did not keep.
+ * The Sol-Attn abstract (listed on the Prism paper page) keeps unselected
+ * blocks in the online softmax approximately, by reusing their proxy
+ * scores, instead of dropping them.  Reading: an unselected block j counts,
+ * for every query row of block i, as its 64 keys all scoring the stage-2
+ * logit z_ij = <qbar_i, kbar_j> / sqrt(d) and all carrying the block's mean
+ * value vbar_j; the kept blocks stay exact; one softmax over both.
+ *
+ * prism_dropped_terms, per query block i, from the stage-2 probabilities
+ * p_ij (reused, not recomputed) and the stage-3 lists:
+ *   s_i        = sum of p_ij over the blocks i did not keep (fp64);
+ *   drop_lse_i = ln 64 + L_i + ln s_i, L_i = ln sum_j exp(z_ij) taken as
+ *                z_ij* - ln p_ij* at the row's largest p (fp64); -inf when
+ *                s_i = 0 (every block kept);
+ *   drop_v_i   = sum over the same blocks of p_ij vbar_j, divided by s_i
+ *                (fp32 products and sums; 0 when s_i = 0).
+ * proxy, q_mean, k_mean : stage-2 outputs, fp64 (proxy [B,Hh,Nb,Nb]).
+ * v, dtype, perm : values [B, Hh, N, d] and the stage-1 permutation.
+ * counts, kv_idx, capacity : stage-3 lists (same contract as the forward).
+ * drop_lse : out [B, Hh, Nb] fp32.   drop_v : out [B, Hh, Nb, d] fp32.
+ * workspace: at least prism_dropped_terms_workspace_bytes() (block means of
+ *            v, fp32, and the two list bitmaps).
+ *
+ * prism_sparse_attn_fwd_corrected: prism_sparse_attn_fwd (same arguments,
+ * same workspace) whose softmax also holds the stand-in.  Per row r of
+ * block i, with o, lse the exact sparse results:
+ *   lse'_r = ln(exp(lse_r) + exp(drop_lse_i)),
+ *   o'_r   = exp(lse_r - lse'_r) o_r + exp(drop_lse_i - lse'_r) drop_v_i,
+ * folded into the kernel's final normalisation (no extra pass over o).  A
+ * row whose drop_lse is -inf gets exactly the prism_sparse_attn_fwd result.
+ * There is no gradient of the stand-in: prism_sparse_attn_bwd differentiates
+ * the exact sparse attention and takes that call's o and lse. */
+size_t prism_dropped_terms_workspace_bytes(int B, int Hh, int N, int d);
+prism_status prism_dropped_terms(const double* proxy, const double* q_mean,
+                                 const double* k_mean, const void* v,
+                                 int dtype, const int32_t* perm,
+                                 const int32_t* counts, const int32_t* kv_idx,
+                                 int capacity, int B, int Hh, int N, int d,
+                                 float* drop_lse, float* drop_v,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+prism_status prism_sparse_attn_fwd_corrected(
+    const void* q, const void* k, const void* v, int dtype,
+    const int32_t* perm, const int32_t* counts, const int32_t* kv_idx,
+    int capacity, int B, int Hh, int N, int d, float softmax_scale,
+    const float* drop_lse, const float* drop_v, void* o, float* lse,
+    void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

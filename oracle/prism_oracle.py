@@ -426,9 +426,9 @@ def sparse_attn_bwd(q, k, v, do, perm, lists, scale: Optional[float] = None,
 def dropped_block_terms(q_mean, k_mean, v_mean, lists):
     """Weight and mean value of the blocks each query block left out (R21).
 
-    Sol-Attn abstract page: instead of discarding unselected blocks, their
-    proxy scores are reused to approximate what they contribute, inside the
-    same online softmax.  Reading: an unselected KV block j counts, for every
+    Sol-Attn abstract (listed on the Prism paper page): instead of
+    discarding unselected blocks, their proxy scores are reused to
+    approximate what they contribute, inside the same online softmax.  Reading: an unselected KV block j counts, for every
     query row of block i, as its 64 keys all scoring the pooled logit
     z_ij = <qbar_i, kbar_j> / sqrt(d) (stage 2's logit) and all carrying the
     block's mean value vbar_j.

@@ -23,7 +23,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = P.lib()
     names = _declared()
-    assert len(names) == 16, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), n
     # the Python binding carries the same names
@@ -165,3 +165,35 @@ def test_misaligned_pointers_rejected():
            256, 128, -1.0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
     _expect(1, P.prism_sparse_attn_bwd, *(bwd[:16] + [FAKE + 4] + bwd[17:]))
     _expect(1, P.prism_sparse_attn_bwd, *(bwd[:19] + [FAKE + 8] + bwd[20:]))
+
+
+def test_dropped_terms_rejections():
+    """The forward-only variant with the stand-in of the unselected blocks:
+    the same host-side checks as the attention calls."""
+    nb = 4500
+    w = P.prism_dropped_terms_workspace_bytes(1, 24, 288000, 128)
+    # block means of v (fp32) and two list bitmaps
+    assert w >= 24 * nb * 128 * 4 + 2 * 24 * nb * ((nb + 31) // 32) * 4
+    assert P.prism_dropped_terms_workspace_bytes(1, 24, 288000, 96) == 0
+    dt = [FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 4, 1, 2, 256, 128,
+          FAKE, FAKE, FAKE, 1 << 30, None]
+    _expect(3, P.prism_dropped_terms, *(dt[:12] + [96] + dt[13:]))
+    _expect(2, P.prism_dropped_terms, *(dt[:11] + [250] + dt[12:]))
+    _expect(2, P.prism_dropped_terms, *(dt[:8] + [3] + dt[9:]))
+    _expect(1, P.prism_dropped_terms, *([None] + dt[1:]))
+    _expect(1, P.prism_dropped_terms, *(dt[:14] + [None] + dt[15:]))
+    _expect(1, P.prism_dropped_terms, *(dt[:4] + [5] + dt[5:]))
+    _expect(1, P.prism_dropped_terms, *(dt[:14] + [FAKE + 4] + dt[15:]))
+    _expect(4, P.prism_dropped_terms, *(dt[:15] + [None] + dt[16:]))
+    _expect(4, P.prism_dropped_terms, *(dt[:16] + [64] + dt[17:]))
+    big = dt[:11] + [64 * 8193] + dt[12:]
+    big[8] = 8193
+    _expect(3, P.prism_dropped_terms, *big)
+    fc = [FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, 4, 1, 2, 256, 128, -1.0,
+          FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None]
+    _expect(1, P.prism_sparse_attn_fwd_corrected, *(fc[:13] + [None] + fc[14:]))
+    _expect(1, P.prism_sparse_attn_fwd_corrected, *(fc[:14] + [None] + fc[15:]))
+    _expect(1, P.prism_sparse_attn_fwd_corrected, *(fc[:14] + [FAKE + 4] + fc[15:]))
+    _expect(3, P.prism_sparse_attn_fwd_corrected, *(fc[:11] + [80] + fc[12:]))
+    _expect(4, P.prism_sparse_attn_fwd_corrected, *(fc[:18] + [16] + fc[19:]))
+    _expect(4, P.prism_sparse_attn_fwd_corrected, *(fc[:17] + [None] + fc[18:]))

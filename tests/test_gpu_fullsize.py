@@ -246,6 +246,46 @@ def test_forward_full_size(cid):
     _check_forward(x, g, perm, routes, nsample=12, bf16=True)
 
 
+def test_corrected_forward_full_size():
+    """The variant with the pooled stand-in of the unselected blocks on the
+    2K grid, all heads in one call: sampled query blocks of one head against
+    the oracle (stand-in terms and corrected rows)."""
+    x = _inputs(3)
+    _print("full-size corrected forward", x.cfg["name"])
+    g = _run_gpu(x, backward=False)
+    v = _dev(x.v)
+    dl, dv = P.dropped_terms(g["proxy"], g["qm"], g["km"], v, g["perm"],
+                             g["counts"], g["kv"])
+    oc, lc = P.sparse_attn_fwd_corrected(_dev(x.q), _dev(x.k), v, g["perm"],
+                                         g["counts"], g["kv"], dl, dv)
+    torch.cuda.synchronize()
+    ref = _oracle_stage1(x)
+    perm = ref["perm"]
+    h = 1
+    routes = _check_routing(x, g, perm, [h])
+    route = routes[h]
+    nb = len(route["counts"])
+    rng = np.random.default_rng(3)
+    good = np.array([i for i in range(nb) if i not in route["bad_rows"]])
+    blocks = sorted(rng.choice(good, size=6, replace=False).tolist())
+    qh, kh, vh = (widen(a[0, h]) for a in (x.q, x.k, x.v))
+    qm = po.pool_blocks(qh, perm)
+    rdl, rdv = po.dropped_block_terms(qm[blocks], po.pool_blocks(kh, perm),
+                                      po.pool_blocks(vh, perm),
+                                      [route["lists"][i] for i in blocks])
+    np.testing.assert_allclose(dl[0, h].cpu().numpy()[blocks], rdl, rtol=1e-6)
+    rel, mx = err_stats(dv[0, h].cpu().numpy()[blocks], rdv)
+    assert rel < 1e-5 and mx < 1e-5, (rel, mx)
+    ro, rl = po.sparse_attn_fwd_corrected(qh, kh, vh, perm, route["lists"],
+                                          query_blocks=blocks)
+    rows = np.concatenate([perm[64 * i:64 * (i + 1)] for i in blocks])
+    r1 = assert_close(oc[0, h].float().cpu().numpy()[rows], ro[rows], True, "o")
+    r2 = assert_close(lc[0, h].cpu().numpy()[rows], rl[rows], True, "lse")
+    share = np.exp(np.repeat(rdl, 64) - rl[rows])     # stand-in's softmax mass
+    _print(f"  drop_v rel {rel:.1e}; corrected o {r1}, lse {r2}; stand-in "
+           f"mass per row {share.min():.3f} .. {share.max():.3f}")
+
+
 @pytest.mark.parametrize("cid", [4, 5])
 def test_training_full_size(cid):
     x = _inputs(cid)
