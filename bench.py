@@ -37,6 +37,7 @@ METRIC = ("effective sparse-attn TFLOP/s fwd+bwd @2K grid; selection GB/s; "
           "MFMA % of peak")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP64_TFLOPS = 78.6       # MI355X fp64 (vector and matrix)
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 (vector and matrix)
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 BLOCK = 64
 
@@ -64,7 +65,8 @@ def parse():
 def kernel_work(name, w):
     """(kind, algorithmic amount per launch) of one library kernel.
 
-    kind "mfma": bf16 FLOPs; "fp64": fp64 FLOPs; "hbm": bytes.
+    kind "mfma": bf16 FLOPs; "fp64": fp64 FLOPs; "fp32": fp32 MFMA FLOPs;
+    "hbm": bytes.
     """
     B, Hh, N, d, Nb, C, sc = (w["B"], w["Hh"], w["N"], w["d"], w["Nb"],
                               w["C"], w["sigma_c"])
@@ -86,6 +88,10 @@ def kernel_work(name, w):
         "bitmap_transpose": ("hbm", 8 * B * Hh * ((Nb + 31) // 32) * Nb),
         "pair_weights": ("hbm", 4 * B * Hh * ((Nb + 31) // 32) * Nb
                          + 4 * 32 * B * Hh * Nb),
+        # forward variant with the stand-in of the unselected blocks
+        "pool_values": ("hbm", B * Hh * N * d * esz + 4 * B * Hh * Nb * d
+                        + 4 * B * Hh * N),
+        "dropped_terms": ("fp32", 2 * B * Hh * Nb * Nb * d),
     }
     return table.get(name, (None, 0))
 
@@ -200,6 +206,79 @@ def cpu_baseline(x, w, counts_host, perm_host, budget_s):
         "stage_seconds_extrapolated": {"zone_shapes": t_stage1,
                                        "pool_proxy_select": t_route,
                                        "attention_fwd_bwd": t_att_full},
+    }
+
+
+# ------------------------------------------------ forward variant (timed apart)
+def bench_dropped_variant(P, args, w, t, dt_code, fwd_plain_ms, stream):
+    """The forward variant that keeps a pooled stand-in of the unselected
+    blocks in the softmax: prism_dropped_terms + prism_sparse_attn_fwd_corrected
+    on the same inputs and routing as the steps, timed after them (it is not
+    part of a training step).  Returns the per-call and per-kernel times and
+    the roofline of the dropped_terms kernel."""
+    import numpy as np
+    import torch
+    B, Hh, N, d, Nb = w["B"], w["Hh"], w["N"], w["d"], w["Nb"]
+    dev = t["q"].device
+    sh = stream.cuda_stream
+    dl = torch.empty((B, Hh, Nb), dtype=torch.float32, device=dev)
+    dv = torch.empty((B, Hh, Nb, d), dtype=torch.float32, device=dev)
+    wsd = torch.empty(P.prism_dropped_terms_workspace_bytes(B, Hh, N, d),
+                      dtype=torch.uint8, device=dev)
+    oc = torch.empty_like(t["q"])
+    lc = torch.empty_like(t["lse"])
+    p = {n: x.data_ptr() for n, x in t.items()}
+
+    def once(ev=None):
+        if ev:
+            ev[0].record(stream)
+        P.prism_dropped_terms(p["proxy"], p["qm"], p["km"], p["v"], dt_code,
+                              p["perm"], p["counts"], p["kv_idx"], Nb, B, Hh,
+                              N, d, dl.data_ptr(), dv.data_ptr(),
+                              wsd.data_ptr(), wsd.numel(), sh)
+        if ev:
+            ev[1].record(stream)
+        P.prism_sparse_attn_fwd_corrected(
+            p["q"], p["k"], p["v"], dt_code, p["perm"], p["counts"],
+            p["kv_idx"], Nb, B, Hh, N, d, -1.0, dl.data_ptr(), dv.data_ptr(),
+            oc.data_ptr(), lc.data_ptr(), p["wsf"], t["wsf"].numel(), sh)
+        if ev:
+            ev[2].record(stream)
+
+    once()
+    torch.cuda.synchronize()
+    reps = max(1, min(args.steps, 3))
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+           for _ in range(reps)]
+    P.prism_profile_enable(1)
+    P.prism_profile_reset()
+    for r in range(reps):
+        once(evs[r])
+    torch.cuda.synchronize()
+    kt = P.kernel_times()
+    P.prism_profile_enable(0)
+    per = {}
+    for name, ms in kt:
+        per.setdefault(name, []).append(ms)
+    kernels = {n: {"avg_ms": float(np.mean(v)), "launches": len(v) / reps}
+               for n, v in per.items()}
+    fl = kernel_work("dropped_terms", w)[1]
+    dt_ms = kernels["dropped_terms"]["avg_ms"]
+    bytes_ = 8 * B * Hh * Nb * Nb + B * Hh * Nb * ((Nb + 31) // 32) * 4 \
+        + 2 * 4 * B * Hh * Nb * d + 4 * B * Hh * Nb
+    roof = {"kernel": "dropped_terms", "avg_launch_ms": dt_ms,
+            "fp32_tflops": fl / (dt_ms * 1e-3) / 1e12,
+            "frac_of_fp32_peak": fl / (dt_ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+            "gbs": bytes_ / (dt_ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": bytes_ / (dt_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "algorithmic_flops": fl, "algorithmic_bytes": bytes_}
+    return {
+        "dropped_terms_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+        "fwd_corrected_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+        "fwd_plain_ms": fwd_plain_ms,
+        "dropped_lse_finite_rows": int(torch.isfinite(dl).sum().item()),
+        "kernels": kernels,
+        "dropped_terms_roofline": roof,
     }
 
 
@@ -411,6 +490,10 @@ def main():
         "stage_ms": stage_ms,
         "kernels": kernels,
     }
+    out["variants"] = {"fwd_with_dropped_stand_in": bench_dropped_variant(
+        P, args, w, dict(q=q, k=k, v=v, perm=perm, qm=qm, km=km, proxy=proxy,
+                         counts=counts, kv_idx=kv_idx, wsf=wsf, lse=lse),
+        dt_code, stage_ms["attn_fwd"], stream)}
     if not args.no_cpu_baseline:
         perm_host = perm.cpu().numpy()
         t0 = time.perf_counter()
