@@ -597,15 +597,20 @@ prism_status launch_select(const double* proxy, int B, int Hh, int Nb,
                            int top_k, double tau, int32_t* counts,
                            int32_t* kv_idx, int capacity, hipStream_t stream) {
   const unsigned rows = (unsigned)((long long)B * Hh * Nb);
-  // keys per thread: the smallest instantiated multiple of 4 covering the row
+  // keys per thread: the smallest instantiated count covering the row (the
+  // 720p, 1080p and 2K grids need 5, 10 and 18: unused key slots still cost
+  // a compare in every pass)
   const int per = (Nb + kThreads - 1) / kThreads;
 #define PRISM_SELECT(NPT_)                                                     \
   PRISM_LAUNCH("select_rows", select_rows<NPT_>, dim3(rows), dim3(kThreads), 0, \
                stream, proxy, Nb, top_k, tau, counts, kv_idx, capacity)
   if (per <= 4) PRISM_SELECT(4);
+  else if (per <= 6) PRISM_SELECT(6);
   else if (per <= 8) PRISM_SELECT(8);
+  else if (per <= 10) PRISM_SELECT(10);
   else if (per <= 12) PRISM_SELECT(12);
   else if (per <= 16) PRISM_SELECT(16);
+  else if (per <= 18) PRISM_SELECT(18);
   else if (per <= 20) PRISM_SELECT(20);
   else if (per <= 24) PRISM_SELECT(24);
   else PRISM_SELECT(32);

@@ -9,10 +9,13 @@
 // "三者如何协同": one of 13 candidate shapes per zone.
 //
 // Kernels (all HBM-streaming except the tiny finaliser):
-//   zone_feat_dev   one workgroup per (zone, 128-byte channel slice): stages
-//                   the zone's slice (<= 512 tokens x 128 B) in LDS with
-//                   coalesced 16-byte loads, then sums squared deviations
-//                   from the line mean along T, H and W lines in fp64.
+//   zone_feat_dev   one workgroup per (zone, 64-byte channel slice): stages
+//                   the zone's slice (<= 512 tokens x 64 B = 32 KB) in LDS
+//                   with 16-byte loads, then sums squared deviations from
+//                   the line mean along T, H and W lines in fp64.  32 KB of
+//                   LDS lets four workgroups share a CU, so one's loads
+//                   overlap the others' arithmetic (128-byte slices: 27%
+//                   slower, two per CU).
 //   token_rms       one wave per token: ||dh||_2 / sqrt(C) in fp64.
 //   zone_finalize   one workgroup per zone: reduces the slices in a fixed
 //                   order, adds the a2v-norm term, takes the cost argmin and
@@ -23,7 +26,7 @@ namespace prism {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowBytes = 128;        // bytes of one token's channel slice
+constexpr int kRowBytes = 64;         // bytes of one token's channel slice
 constexpr int kMaxZoneTokens = 512;   // zone extents <= 8
 
 struct ZoneBox {
@@ -111,16 +114,17 @@ __global__ __launch_bounds__(kThreads) void zone_feat_dev(
   const int c0 = slice * CH;
   const int valid_bytes = min(CH, C - c0) * (int)sizeof(E);  // multiple of 16
 
-  // stage: 8 threads per token row, 16 bytes each; every load of the thread
-  // is issued before the first LDS store, so a workgroup keeps its whole
-  // slice (up to 64 KB) in flight
-  constexpr int kIter = kMaxZoneTokens * 8 / kThreads;
+  // stage: kPieces threads per token row, 16 bytes each; every load of the
+  // thread is issued before the first LDS store, so a workgroup keeps its
+  // whole slice (up to 32 KB) in flight
+  constexpr int kPieces = kRowBytes / 16;
+  constexpr int kIter = kMaxZoneTokens * kPieces / kThreads;
   const unsigned char* fb = feat + (long long)b * N * rowB + (long long)c0 * sizeof(E);
   uint4 v[kIter];
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
     const int i = threadIdx.x + it * kThreads;
-    const int tok = i >> 3, piece = i & 7;
+    const int tok = i / kPieces, piece = i % kPieces;
     v[it] = make_uint4(0, 0, 0, 0);
     if (tok < nt && piece * 16 < valid_bytes) {
       const int lw = tok % zb.Lw, lh = (tok / zb.Lw) % zb.Lh, lt = tok / (zb.Lw * zb.Lh);
@@ -132,8 +136,8 @@ __global__ __launch_bounds__(kThreads) void zone_feat_dev(
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
     const int i = threadIdx.x + it * kThreads;
-    if ((i >> 3) < nt)
-      *reinterpret_cast<uint4*>(tile + (i >> 3) * kRowBytes + (i & 7) * 16) = v[it];
+    if (i / kPieces < nt)
+      *reinterpret_cast<uint4*>(tile + (i / kPieces) * kRowBytes + (i % kPieces) * 16) = v[it];
   }
   __syncthreads();
 
