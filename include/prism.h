@@ -15,7 +15,10 @@
  * "三者如何协同：一步去噪里发生了什么"; the "Prism: Dynamic Sparse
  * Attention for Native 2K Joint Video-Audio Generation Model Training"
  * abstract page (block proxy scores, cumulative-mass selection, online
- * softmax over selected blocks).
+ * softmax over selected blocks).  A forward-only variant keeps the
+ * unselected blocks in the softmax as pooled stand-ins built from the proxy
+ * scores (prism_dropped_terms, prism_sparse_attn_fwd_corrected; the Sol-Attn
+ * abstract listed on that page).
  *
  * Conventions shared by every call
  *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
