@@ -12,10 +12,10 @@
 //   zone_feat_dev   one workgroup per (zone, 64-byte channel slice): stages
 //                   the zone's slice (<= 512 tokens x 64 B = 32 KB) in LDS
 //                   with 16-byte loads, then sums squared deviations from
-//                   the line mean along T, H and W lines in fp64.  32 KB of
-//                   LDS lets four workgroups share a CU, so one's loads
-//                   overlap the others' arithmetic (128-byte slices: 27%
-//                   slower, two per CU).
+//                   the line mean along T, H and W lines in fp64 (bf16:
+//                   exact per-line sums and sums of squares, two channels
+//                   per LDS read).  32 KB of LDS lets four workgroups share
+//                   a CU, so one's loads overlap the others' arithmetic.
 //   token_rms       one wave per token: ||dh||_2 / sqrt(C) in fp64.
 //   zone_finalize   one workgroup per zone: reduces the slices in a fixed
 //                   order, adds the a2v-norm term, takes the cost argmin and
@@ -141,23 +141,56 @@ __global__ __launch_bounds__(kThreads) void zone_feat_dev(
   }
   __syncthreads();
 
-  // compute: thread -> (channel c, line group grp)
-  constexpr int G = kThreads / CH;
-  const int c = threadIdx.x % CH;
-  const int grp = threadIdx.x / CH;
-  const unsigned char* base = tile + c * sizeof(E);
+  // Sums of squared deviations along T, H, W lines, summed over the
+  // slice's channels, reduced over the workgroup.
   double dT = 0.0, dH = 0.0, dW = 0.0;
-  // W lines: (lt, lh)
-  for (int l = grp; l < zb.Lt * zb.Lh; l += G)
-    dW += line_dev<E>(base, zb.Lw, l * zb.Lw, 1);
-  // H lines: (lt, lw)
-  for (int l = grp; l < zb.Lt * zb.Lw; l += G) {
-    const int lt = l / zb.Lw, lw = l % zb.Lw;
-    dH += line_dev<E>(base, zb.Lh, lt * zb.Lh * zb.Lw + lw, zb.Lw);
+  if constexpr (sizeof(E) == 2) {
+    // bf16: a line of <= 8 values has an exact sum s and an exact sum of
+    // squares q in fp64 (8-bit significands), and q - s^2 / L is its squared
+    // deviation, exact up to the final rounding (no cancellation is lost:
+    // both terms are exact).  One LDS read per value and axis, two channels
+    // per 32-bit read.
+    constexpr int CP = kRowBytes / 4;          // channel pairs per slice
+    constexpr int G = kThreads / CP;           // line groups
+    const int cp = threadIdx.x % CP, grp = threadIdx.x / CP;
+    const unsigned char* base = tile + cp * 4;
+    auto line = [&](int tok0, int stride, int L) __attribute__((always_inline)) -> double {
+      double s0 = 0.0, s1 = 0.0, q0 = 0.0, q1 = 0.0;
+      for (int i = 0; i < L; ++i) {
+        const uint32_t u =
+            *reinterpret_cast<const uint32_t*>(base + (tok0 + i * stride) * kRowBytes);
+        const double x0 = (double)__uint_as_float(u << 16);
+        const double x1 = (double)__uint_as_float(u & 0xffff0000u);
+        s0 += x0;
+        s1 += x1;
+        q0 = fma(x0, x0, q0);
+        q1 = fma(x1, x1, q1);
+      }
+      const double invL = 1.0 / (double)L;
+      return (q0 - s0 * s0 * invL) + (q1 - s1 * s1 * invL);
+    };
+    for (int l = grp; l < zb.Lt * zb.Lh; l += G)          // W lines (lt, lh)
+      dW += line(l * zb.Lw, 1, zb.Lw);
+    for (int l = grp; l < zb.Lt * zb.Lw; l += G)          // H lines (lt, lw)
+      dH += line((l / zb.Lw) * zb.Lh * zb.Lw + l % zb.Lw, zb.Lw, zb.Lh);
+    for (int l = grp; l < zb.Lh * zb.Lw; l += G)          // T lines (lh, lw)
+      dT += line(l, zb.Lh * zb.Lw, zb.Lt);
+  } else {
+    // fp32: two passes per line (mean, then squared deviations): wider
+    // inputs do not have exact squares
+    constexpr int G = kThreads / CH;
+    const int c = threadIdx.x % CH;
+    const int grp = threadIdx.x / CH;
+    const unsigned char* base = tile + c * sizeof(E);
+    for (int l = grp; l < zb.Lt * zb.Lh; l += G)          // W lines (lt, lh)
+      dW += line_dev<E>(base, zb.Lw, l * zb.Lw, 1);
+    for (int l = grp; l < zb.Lt * zb.Lw; l += G) {        // H lines (lt, lw)
+      const int lt = l / zb.Lw, lw = l % zb.Lw;
+      dH += line_dev<E>(base, zb.Lh, lt * zb.Lh * zb.Lw + lw, zb.Lw);
+    }
+    for (int l = grp; l < zb.Lh * zb.Lw; l += G)          // T lines (lh, lw)
+      dT += line_dev<E>(base, zb.Lt, l, zb.Lh * zb.Lw);
   }
-  // T lines: (lh, lw)
-  for (int l = grp; l < zb.Lh * zb.Lw; l += G)
-    dT += line_dev<E>(base, zb.Lt, l, zb.Lh * zb.Lw);
 
   dT = wave_sum(dT);
   dH = wave_sum(dH);
