@@ -104,7 +104,14 @@ __global__ __launch_bounds__(kThreads) void zone_feat_dev(
   __shared__ __align__(16) unsigned char tile[kMaxZoneTokens * kRowBytes];
   __shared__ double red[3][kThreads / 64];
 
-  const int slice = blockIdx.x;
+  // the two 64-byte halves of a 128-byte line go to workgroups 8 apart in
+  // launch order (workgroups are dealt round-robin to the 8 XCDs): the same
+  // XCD at about the same time, so the second half is an L2 hit and every
+  // line is fetched once
+  const int bx = blockIdx.x;
+  const int slice = (bx / 16) * 16 + 15 < n_slices
+                        ? (bx / 16) * 16 + 2 * (bx % 8) + (bx / 8) % 2
+                        : bx;
   const int z = blockIdx.y;
   const int b = blockIdx.z;
   const ZoneBox zb = zone_box(g, z);
