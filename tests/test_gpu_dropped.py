@@ -83,3 +83,52 @@ def test_corrected_forward_with_every_block_kept_is_the_plain_forward(grid):
     dl, dv, oc, lc, o, l = _run(c)
     assert torch.isneginf(dl).all() and (dv == 0).all()
     assert torch.equal(oc, o) and torch.equal(lc, l)
+
+
+def test_corrected_forward_max_block_count():
+    """Nb = 8192 (the largest supported): the stand-in terms stream 256
+    bitmap words per row; one query block keeps every block, the others a
+    few; sampled rows against the oracle."""
+    from synth import iid_normal
+    from tests.test_gpu_parity import _two_perms
+    T, H, W = 32, 128, 128
+    N = T * H * W
+    nb = N // 64
+    assert nb == 8192
+    rng = np.random.default_rng(4096)
+    d = 128
+    q, k, v = (iid_normal((1, 1, N, d), seed=s, dtype="bf16", scale=2.0)
+               for s in (91, 92, 93))
+    perm = _two_perms(T, H, W)[1:2]
+    counts = np.zeros((1, 1, nb), dtype=np.int32)
+    kv = np.full((1, 1, nb, nb), -1, dtype=np.int32)
+    lists = []
+    for i in range(nb):
+        L = (np.arange(nb) if i == 0 else
+             np.sort(rng.choice(nb, size=int(rng.integers(1, 17)), replace=False)))
+        counts[0, 0, i] = len(L)
+        kv[0, 0, i, :len(L)] = L
+        lists.append(L)
+    _print("corrected fwd, max blocks", nb)
+    c = dict(q=q, k=k, v=v, perm=perm, counts=counts, kv=kv)
+    dl, dv, oc, lc, o, l = _run(c)
+    dl, dv, lc, l = (t.cpu().numpy() for t in (dl, dv, lc, l))
+    oc, o = to_host(oc), to_host(o)
+    pm = perm[0]
+    q0, k0, v0 = (widen(a[0, 0]) for a in (q, k, v))
+    blocks = [0, 1, 5000, 8191]
+    qm = po.pool_blocks(q0, pm)
+    rdl, rdv = po.dropped_block_terms(qm[blocks], po.pool_blocks(k0, pm),
+                                      po.pool_blocks(v0, pm),
+                                      [lists[i] for i in blocks])
+    assert np.isneginf(dl[0, 0, 0]) and np.isneginf(rdl[0])
+    np.testing.assert_allclose(dl[0, 0][blocks[1:]], rdl[1:], rtol=1e-6)
+    rel, mx = err_stats(dv[0, 0][blocks], rdv)
+    assert rel < 1e-5 and mx < 1e-5, (rel, mx)
+    ro, rl = po.sparse_attn_fwd_corrected(q0, k0, v0, pm, lists,
+                                          query_blocks=blocks)
+    rows = np.concatenate([pm[64 * i:64 * (i + 1)] for i in blocks])
+    assert_close(oc[0, 0][rows], ro[rows], True, "o corrected")
+    assert_close(lc[0, 0][rows], rl[rows], True, "lse corrected")
+    rows0 = pm[:64]
+    assert np.array_equal(oc[0, 0][rows0], o[0, 0][rows0])
