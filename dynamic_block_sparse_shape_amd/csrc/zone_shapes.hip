@@ -152,11 +152,14 @@ __global__ __launch_bounds__(kThreads) void zone_feat_dev(
   // slice's channels, reduced over the workgroup.
   double dT = 0.0, dH = 0.0, dW = 0.0;
   if constexpr (sizeof(E) == 2) {
-    // bf16: a line of <= 8 values has an exact sum s and an exact sum of
-    // squares q in fp64 (8-bit significands), and q - s^2 / L is its squared
-    // deviation, exact up to the final rounding (no cancellation is lost:
-    // both terms are exact).  One LDS read per value and axis, two channels
-    // per 32-bit read.
+    // bf16: the squared deviation of a line of L <= 8 values is
+    // q - s^2 / L with s the sum and q the sum of squares.  With 8-bit
+    // significands, s and q are exact in fp64 whenever the line's values lie
+    // within 2^17 of each other in magnitude -- the near-constant lines where
+    // the subtraction cancels -- so the result is then exact up to its final
+    // rounding; a line with a wider spread has a deviation of the order of q
+    // itself.  One LDS read per value and axis, two channels per 32-bit
+    // read.
     constexpr int CP = kRowBytes / 4;          // channel pairs per slice
     constexpr int G = kThreads / CP;           // line groups
     const int cp = threadIdx.x % CP, grp = threadIdx.x / CP;
