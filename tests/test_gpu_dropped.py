@@ -72,6 +72,35 @@ def test_dropped_terms_and_corrected_forward(dtype, d):
     assert changed > 1e-2          # the stand-in does change the other rows
 
 
+@pytest.mark.parametrize("grid", [(4, 4, 8), (4, 4, 12), (4, 8, 16)])
+def test_corrected_forward_tiny_block_counts(grid):
+    """2, 3 and 8 blocks per head (one 32-column proxy slice, partly empty;
+    one 64-row tile, mostly empty): rows that keep one block and rows that
+    keep all."""
+    T, H, W = grid
+    c = _attn_case("bf16", 128, T=T, H=H, W=W, seed=13)
+    _print("corrected fwd tiny", grid)
+    dl, dv, oc, lc, o, l = _run(c)
+    dl, dv, lc = (t.cpu().numpy() for t in (dl, dv, lc))
+    oc = to_host(oc)
+    for b in range(c["B"]):
+        perm = c["perm"][b]
+        for h in range(c["Hh"]):
+            qh, kh, vh = (widen(c[n][b, h]) for n in ("q", "k", "v"))
+            lists = c["lists"][b][h]
+            rdl, rdv = po.dropped_block_terms(po.pool_blocks(qh, perm),
+                                              po.pool_blocks(kh, perm),
+                                              po.pool_blocks(vh, perm), lists)
+            fin = np.isfinite(rdl)
+            assert np.array_equal(np.isfinite(dl[b, h]), fin)
+            np.testing.assert_allclose(dl[b, h][fin], rdl[fin], rtol=1e-6, atol=1e-6)
+            rel, mx = err_stats(dv[b, h], rdv)
+            assert rel < 1e-5 and mx < 1e-5, ("drop_v", b, h, rel, mx)
+            ro, rl = po.sparse_attn_fwd_corrected(qh, kh, vh, perm, lists)
+            assert_close(oc[b, h], ro, True, f"o corrected [{b},{h}]")
+            assert_close(lc[b, h], rl, True, f"lse corrected [{b},{h}]")
+
+
 @pytest.mark.parametrize("grid", [(1, 8, 8), (4, 4, 12), (20, 18, 24)])
 def test_corrected_forward_with_every_block_kept_is_the_plain_forward(grid):
     T, H, W = grid
