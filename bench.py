@@ -62,20 +62,34 @@ def parse():
     return ap.parse_args()
 
 
+# Matrix products each backward kernel executes per selected pair, in units
+# of 64*64*d FLOP (one 64x64xd product is 2 units): dK/dV recomputes S and dP
+# and forms dV, dK (8); dQ recomputes S and dP and forms dQ (6).  The
+# algorithmic backward is 10 units per pair (S, dP, dV, dQ, dK, each once),
+# so each kernel is credited its executed share of those 10.
+BWD_UNITS = 10
+BWD_EXEC_UNITS = {"dkdv_bf16": 8, "dq_bf16": 6}
+
+
 def kernel_work(name, w):
     """(kind, algorithmic amount per launch) of one library kernel.
 
     kind "mfma": bf16 FLOPs; "fp64": fp64 FLOPs; "fp32": fp32 MFMA FLOPs;
-    "hbm": bytes.
+    "hbm": bytes.  The forward counts 4*64^2*d FLOP per selected pair; the
+    backward 10*64^2*d per pair, split between dK/dV and dQ in proportion to
+    the products each executes (BWD_EXEC_UNITS).
     """
     B, Hh, N, d, Nb, C, sc = (w["B"], w["Hh"], w["N"], w["d"], w["Nb"],
                               w["C"], w["sigma_c"])
     pair = BLOCK * BLOCK * d                    # one 64x64xd product = 2*pair
     esz = 2
+    exec_total = sum(BWD_EXEC_UNITS.values())
     table = {
         "attn_fwd_bf16": ("mfma", 4 * pair * sc),
-        "dkdv_bf16": ("mfma", 8 * pair * sc),
-        "dq_bf16": ("mfma", 6 * pair * sc),
+        "dkdv_bf16": ("mfma", BWD_UNITS * BWD_EXEC_UNITS["dkdv_bf16"]
+                      / exec_total * pair * sc),
+        "dq_bf16": ("mfma", BWD_UNITS * BWD_EXEC_UNITS["dq_bf16"]
+                    / exec_total * pair * sc),
         "proxy_logits": ("fp64", 2 * B * Hh * Nb * Nb * d),
         "select_rows": ("hbm", 8 * B * Hh * Nb * Nb + 4 * sc + 4 * B * Hh * Nb),
         "row_softmax": ("hbm", 16 * B * Hh * Nb * Nb),
@@ -424,6 +438,12 @@ def main():
         if kind == "mfma":
             rec["tflops"] = amount / (avg * 1e-3) / 1e12
             rec["frac_of_bf16_peak"] = rec["tflops"] / PEAK_BF16_TFLOPS
+            if name in BWD_EXEC_UNITS:
+                # products the kernel actually runs (recomputed S, dP included)
+                ex = BWD_EXEC_UNITS[name] * BLOCK * BLOCK * d * sigma_c
+                rec["executed_mfma_tflops"] = ex / (avg * 1e-3) / 1e12
+                rec["executed_frac_of_bf16_peak"] = (
+                    rec["executed_mfma_tflops"] / PEAK_BF16_TFLOPS)
         elif kind == "fp64":
             rec["tflops_fp64"] = amount / (avg * 1e-3) / 1e12
             rec["frac_of_fp64_peak"] = rec["tflops_fp64"] / PEAK_FP64_TFLOPS
@@ -456,6 +476,10 @@ def main():
     roof["kernel"] = dom
     roof["avg_launch_ms"] = dom_ms
     roof["algorithmic_per_launch"] = amount
+    if dom in BWD_EXEC_UNITS:
+        roof["algorithmic_rule"] = (
+            f"backward 10*64^2*d FLOP per selected pair, {dom} credited "
+            f"{BWD_EXEC_UNITS[dom]}/{sum(BWD_EXEC_UNITS.values())} of it")
 
     out = {
         "metric": METRIC,
@@ -480,6 +504,9 @@ def main():
         "attn_fwd_tflops": kernels.get("attn_fwd_bf16", {}).get("tflops"),
         "attn_fwd_bwd_tflops_stage4": (flops_fwd + flops_bwd) /
         ((stage_ms["attn_fwd"] + stage_ms["attn_bwd"]) * 1e-3) / 1e12,
+        "attn_bwd_tflops": flops_bwd / (stage_ms["attn_bwd"] * 1e-3) / 1e12,
+        "attn_bwd_frac_of_bf16_peak": flops_bwd / (stage_ms["attn_bwd"] * 1e-3)
+        / 1e12 / PEAK_BF16_TFLOPS,
         "mfma_frac": {n: r.get("frac_of_bf16_peak") for n, r in kernels.items()
                       if "frac_of_bf16_peak" in r},
         "density": sigma_c / (B * Hh * Nb * Nb),

@@ -413,7 +413,9 @@ __global__ __launch_bounds__(512, 2) void dq_bf16(
   const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(k, head, N);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(v, head, N);
   uint32_t offs_n[SH::kPerThread];
-  const int last = ucnt - 1;
+  // an empty union leaves ulist[0] = block 0 (pair_union): a safe id for
+  // the prologue's loads, and the loop runs no step (dq = 0)
+  const int last = max(ucnt - 1, 0);
   auto uid = [&](int t) __attribute__((always_inline)) -> int {
     return (int)(ulist[min(t, last)] & 0xffffu);
   };
@@ -534,10 +536,13 @@ __global__ __launch_bounds__(64) void dq_f32(
   for (int e = 0; e < D; ++e) acc[e] = 0.f;
   const float L = lse[qr], Dl = delta[qr];
   const long long rowid = ((long long)b * Hh + h) * Nb + i;
-  const int cnt = counts[rowid];
+  // counts clamped to [0, Nb], ids outside [0, Nb) skipped, as the column
+  // bitmap that dkdv_f32 reads does
+  const int cnt = min(max(counts[rowid], 0), Nb);
   const int32_t* lst = kv_idx + rowid * (long long)capacity;
   for (int t = 0; t < cnt; ++t) {
     const int j = lst[t];
+    if ((unsigned)j >= (unsigned)Nb) continue;
     for (int r = 0; r < 64; ++r) {
       const long long kr = head + pb[64 * j + r];
       float s = 0.f, dpv = 0.f;

@@ -99,7 +99,9 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
   const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(k, head, N);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(v, head, N);
   uint32_t offs_n[SH::kPerThread];
-  const int last = ucnt - 1;
+  // an empty union leaves ulist[0] = block 0 (pair_union), a safe id for
+  // the prologue's loads; the loop then runs no step
+  const int last = max(ucnt - 1, 0);
   auto uid = [&](int t) __attribute__((always_inline)) -> int {
     return (int)(ulist[min(t, last)] & 0xffffu);
   };
@@ -221,7 +223,10 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
   if (kh == 0 && (half == 0 || has_second)) {
     const float m2 = sm_m[half][qh][c], l2 = sm_l[half][qh][c];
     float m = fmaxf(m_run, m2);
-    const float a1 = exp2_fast(m_run - m), a2 = exp2_fast(m2 - m);
+    // m = -inf: the query block's list is empty (no key at all)
+    const bool none = m == -INFINITY;
+    const float a1 = none ? 0.f : exp2_fast(m_run - m);
+    const float a2 = none ? 0.f : exp2_fast(m2 - m);
     float l = l_run * a1 + l2 * a2;
     // optional stand-in of the blocks this query block did not keep: weight
     // exp(drop_lse) (natural log) with value drop_v, one more term of the
@@ -231,13 +236,14 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
     if (drop_lse != nullptr) {
       const float dl = drop_lse[bh * Nb + iq] * kLog2e;
       const float mm = fmaxf(m, dl);
-      b1 = exp2_fast(m - mm);
-      b2 = exp2_fast(dl - mm);
+      b1 = none ? 0.f : exp2_fast(m - mm);
+      b2 = dl == -INFINITY ? 0.f : exp2_fast(dl - mm);
       m = mm;
       l = l * b1 + b2;
       dvr = drop_v + (bh * Nb + iq) * D;
     }
-    const float inv_l = 1.f / l;
+    // no key and no stand-in: o = 0, lse = -inf
+    const float inv_l = l > 0.f ? 1.f / l : 0.f;
     uint16_t* orow = o + (head + qrow) * D;
 #pragma unroll
     for (int mt = 0; mt < DT; ++mt)
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
         pk.y = cvt2(vals[2], vals[3]);
         *reinterpret_cast<uint2*>(orow + 32 * mt + 8 * a + 4 * hf) = pk;
       }
-    if (hf == 0) lse[head + qrow] = (m + log2f(l)) * kLn2;
+    if (hf == 0) lse[head + qrow] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -283,10 +289,12 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(
   }
   float m_run = -INFINITY, l_run = 0.f;
   const long long rowid = ((long long)b * Hh + h) * Nb + i;
-  const int cnt = counts[rowid];
+  // counts are clamped to [0, Nb]; ids outside [0, Nb) are skipped
+  const int cnt = min(max(counts[rowid], 0), Nb);
   const int32_t* lst = kv_idx + rowid * (long long)capacity;
   for (int t = 0; t < cnt; ++t) {
     const int j = lst[t];
+    if ((unsigned)j >= (unsigned)Nb) continue;
     for (int r = 0; r < 64; ++r) {
       const long long kr = head + pb[64 * j + r];
       float s = 0.f;
@@ -306,20 +314,22 @@ __global__ __launch_bounds__(64) void attn_fwd_f32(
     // stand-in of the blocks this query block did not keep
     const float dl = drop_lse[rowid];
     const float mm = fmaxf(m_run, dl);
-    const float b1 = expf(m_run - mm), b2 = expf(dl - mm);
+    const float b1 = m_run == -INFINITY ? 0.f : expf(m_run - mm);
+    const float b2 = dl == -INFINITY ? 0.f : expf(dl - mm);
     const float l = l_run * b1 + b2;
     const float* dvr = drop_v + rowid * D;
-    const float inv_l = 1.f / l;
+    const float inv_l = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int e = 0; e < D; ++e)
       o[(head + qrow) * D + e] = (acc[e] * b1 + b2 * dvr[e]) * inv_l;
-    lse[head + qrow] = mm + logf(l);
+    lse[head + qrow] = l > 0.f ? mm + logf(l) : -INFINITY;
     return;
   }
-  const float inv_l = 1.f / l_run;
+  // an empty list: o = 0, lse = -inf
+  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
   for (int e = 0; e < D; ++e) o[(head + qrow) * D + e] = acc[e] * inv_l;
-  lse[head + qrow] = m_run + logf(l_run);
+  lse[head + qrow] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
 }
 
 }  // namespace

@@ -296,8 +296,10 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int s) {
 // Ascending union of two blocks' KV lists, built by a 512-thread workgroup.
 // Each entry is id | (in list 0) << 16 | (in list 1) << 17.  bits holds
 // 2 * ceil(Nb / 32) words and ulist Nb entries (LDS); s_cnt 8 ints.
-// Lists hold distinct ids in [0, Nb), Nb <= 8192.  Returns the union size;
-// ends with a barrier.
+// Nb <= 8192.  Counts are clamped to [0, Nb], ids outside [0, Nb) are
+// skipped and duplicates merge, so any list gives a valid union.  Returns
+// the union size; when it is 0, ulist[0] holds block 0 with no membership
+// bits (a safe id for the gather prologue).  Ends with a barrier.
 __device__ __forceinline__ int pair_union(const int32_t* __restrict__ lst0,
                                           int cnt0,
                                           const int32_t* __restrict__ lst1,
@@ -307,13 +309,16 @@ __device__ __forceinline__ int pair_union(const int32_t* __restrict__ lst0,
   const int wave = tid >> 6, lane = tid & 63;
   for (int w = tid; w < 2 * words; w += 512) bits[w] = 0u;
   __syncthreads();
+  cnt0 = min(max(cnt0, 0), Nb);
+  cnt1 = min(max(cnt1, 0), Nb);
   for (int t = tid; t < cnt0; t += 512) {
     const int j = lst0[t];
-    atomicOr(&bits[j >> 5], 1u << (j & 31));
+    if ((unsigned)j < (unsigned)Nb) atomicOr(&bits[j >> 5], 1u << (j & 31));
   }
   for (int t = tid; t < cnt1; t += 512) {
     const int j = lst1[t];
-    atomicOr(&bits[words + (j >> 5)], 1u << (j & 31));
+    if ((unsigned)j < (unsigned)Nb)
+      atomicOr(&bits[words + (j >> 5)], 1u << (j & 31));
   }
   __syncthreads();
   // thread w owns bitmap word w (words <= 256)
@@ -342,6 +347,7 @@ __device__ __forceinline__ int pair_union(const int32_t* __restrict__ lst0,
                    (((wb >> bit) & 1u) << 17);
     wu &= wu - 1u;
   }
+  if (ucnt == 0 && tid == 0) ulist[0] = 0u;
   __syncthreads();
   return ucnt;
 }

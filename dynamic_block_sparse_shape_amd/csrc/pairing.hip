@@ -40,7 +40,9 @@ __device__ __forceinline__ int cand_of(int i, int c) {
 // holds bit i - 32 w for every query block i in [32 w, 32 w + 32) that
 // selected KV block j.  One workgroup per (bh, w) ORs its 32 lists (any
 // order) into an LDS row of Nb words and writes the row out whole (no
-// global atomics, no clearing pass).
+// global atomics, no clearing pass).  A count is clamped to [0, Nb] and an
+// id outside [0, Nb) is skipped, so a list that breaks the caller contract
+// cannot write outside the LDS row; duplicate ids set the same bit.
 __global__ __launch_bounds__(256) void bitmap_build(
     const int32_t* __restrict__ counts, const int32_t* __restrict__ kv_idx,
     int capacity, int Nb, int words, uint32_t* __restrict__ bits) {
@@ -54,9 +56,12 @@ __global__ __launch_bounds__(256) void bitmap_build(
     const int i = 32 * w + r;
     if (i >= Nb) break;
     const long long row = bh * Nb + i;
-    const int cnt = counts[row];
+    const int cnt = min(max(counts[row], 0), Nb);
     const int32_t* lst = kv_idx + row * (long long)capacity;
-    for (int t = lane; t < cnt; t += 64) atomicOr(&srow[lst[t]], 1u << r);
+    for (int t = lane; t < cnt; t += 64) {
+      const int j = lst[t];
+      if ((unsigned)j < (unsigned)Nb) atomicOr(&srow[j], 1u << r);
+    }
   }
   __syncthreads();
   uint32_t* out = bits + (bh * words + w) * (long long)Nb;

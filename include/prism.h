@@ -174,10 +174,16 @@ prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
  *
  * q, k, v : [B, Hh, N, d] dtype (bf16: MFMA path with fp32 accumulation;
  *           fp32: reference-precision path).
- * perm, counts, kv_idx, capacity : from stages 1 and 3.  Every count must be
- *           in [1, Nb], every listed id in [0, Nb) and the ids of one row
+ * perm, counts, kv_idx, capacity : from stages 1 and 3.  Every count should
+ *           be in [1, Nb], every listed id in [0, Nb) and the ids of one row
  *           distinct, in any order (caller's contract; stage 3 output
- *           satisfies it).  The bf16 path processes query blocks in pairs
+ *           satisfies it).  The lists live in device memory, so the host
+ *           cannot check them; the kernels clamp each count to [0, Nb] and
+ *           skip ids outside [0, Nb), so a list that breaks the contract
+ *           never makes them read or write out of bounds.  A query block
+ *           with no valid id gets o = 0 and lse = -inf (no key to attend
+ *           to).  Duplicate ids count once in the bf16 path and once per
+ *           copy in the fp32 path.  The bf16 path processes query blocks in pairs
  *           over the union of their lists: neighbours (within 16 places in
  *           the permuted order) whose lists overlap most, matched on the
  *           device from the lists in every call; results do not depend on
@@ -209,6 +215,9 @@ prism_status prism_sparse_attn_fwd(const void* q, const void* k,
  * q, k, v, o, d_o : [B, Hh, N, d] dtype; lse [B, Hh, N] fp32 from the
  *                   forward.
  * dq, dk, dv      : out [B, Hh, N, d] fp32, raster order (fully written).
+ *                   Lists are read as in the forward (counts clamped, ids
+ *                   outside [0, Nb) skipped); a query block with no valid
+ *                   id gets dq = 0 and adds nothing to dk, dv.
  * workspace       : at least prism_sparse_attn_bwd_workspace_bytes() (D
  *                   rows, list bitmaps, and the pairings of KV blocks and
  *                   of query blocks, as in the forward). */

@@ -262,11 +262,15 @@ def test_stage4_forward(dtype, d):
             _print("  o", r1, "lse", r2)
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64),
-                                     ("fp32", 64)])
-def test_stage4_backward(dtype, d):
-    c = _attn_case(dtype, d, seed=7)
-    _print("bwd", dtype, d)
+@pytest.mark.parametrize("dtype,d,maxc", [("bf16", 128, 12), ("bf16", 64, 12),
+                                          ("fp32", 64, 12), ("fp32", 128, 12),
+                                          ("bf16", 128, None), ("bf16", 64, None)])
+def test_stage4_backward(dtype, d, maxc):
+    """Every row of dQ, dK, dV against the oracle.  maxc=None draws list
+    lengths up to Nb, so every KV block is selected by about half of the 135
+    query blocks and the dK / dV kernel walks long column unions."""
+    c = _attn_case(dtype, d, seed=7, maxc=maxc)
+    _print("bwd", dtype, d, maxc)
     args = [to_dev(c[n]) for n in ("q", "k", "v")]
     perm, counts, kv = to_dev(c["perm"]), to_dev(c["counts"]), to_dev(c["kv"])
     o, lse = P.sparse_attn_fwd(*args, perm, counts, kv)
@@ -454,3 +458,63 @@ def test_pipeline_tiny_fp32_config():
         ro, rl = po.sparse_attn_fwd(rq, rk, rv, rperm, route["lists"])
         assert_close(o[0, h].cpu().numpy(), ro, False, "o")
         assert_close(lse[0, h].cpu().numpy(), rl, False, "lse")
+
+
+def test_stage4_lists_outside_the_contract():
+    """Lists the host cannot check (they live in device memory): a count of
+    0, a count above Nb, ids outside [0, Nb) and duplicate ids.  The kernels
+    clamp counts to [0, Nb], skip invalid ids and (bf16) merge duplicates:
+    results equal those of the cleaned lists, a block with no valid id gets
+    o = 0, lse = -inf, dq = 0 and adds nothing to dk, dv."""
+    T, H, W = 20, 18, 24
+    c = _attn_case("bf16", 128, T=T, H=H, W=W, B=1, Hh=2, seed=21, maxc=20)
+    nb = c["N"] // 64
+    counts, kv = c["counts"].copy(), c["kv"].copy()
+    clean = [list(L) for L in c["lists"][0]]
+    # head 0: block 3 empty, block 4 with every id invalid, block 5 with a
+    # count above Nb over a row padded with invalid ids; head 1: invalid and
+    # duplicate ids mixed into valid lists
+    counts[0, 0, 3] = 0
+    clean[0][3] = []
+    counts[0, 0, 4] = 3
+    kv[0, 0, 4, :3] = [-1, nb, 1 << 20]
+    clean[0][4] = []
+    L5 = list(clean[0][5])
+    kv[0, 0, 5, :] = -7
+    kv[0, 0, 5, :len(L5)] = L5
+    counts[0, 0, 5] = nb + 50
+    for i in (6, 7, 8):
+        L = list(c["lists"][0][1][i])
+        row = [L[0], -3, L[0], nb + 1] + L[1:] + [L[-1]]
+        kv[0, 1, i, :len(row)] = row
+        counts[0, 1, i] = len(row)
+    _print("lists outside the contract")
+    args = [to_dev(c[n]) for n in ("q", "k", "v")]
+    perm, dcounts, dkv = to_dev(c["perm"]), to_dev(counts), to_dev(kv)
+    o, lse = P.sparse_attn_fwd(*args, perm, dcounts, dkv)
+    dq, dk, dv = P.sparse_attn_bwd(*args, o, to_dev(c["do"]), lse, perm,
+                                   dcounts, dkv)
+    torch.cuda.synchronize()
+    o, lse = to_host(o), lse.cpu().numpy()
+    dq, dk, dv = (t.cpu().numpy() for t in (dq, dk, dv))
+    pm = c["perm"][0]
+    for h in range(2):
+        qq, kk, vv, dd = (widen(c[n][0, h]) for n in ("q", "k", "v", "do"))
+        lists = [np.array(sorted(set(L)), dtype=np.int64) for L in clean[h]]
+        live = [i for i in range(nb) if len(lists[i])]
+        dead = [i for i in range(nb) if not len(lists[i])]
+        ro, rl = po.sparse_attn_fwd(qq, kk, vv, pm, lists, query_blocks=live)
+        rdq, rdk, rdv = po.sparse_attn_bwd(qq, kk, vv, dd, pm, lists,
+                                           query_blocks=live)
+        rows = np.concatenate([pm[64 * i:64 * (i + 1)] for i in live])
+        assert_close(o[0, h][rows], ro[rows], True, f"o head {h}")
+        assert_close(lse[0, h][rows], rl[rows], True, f"lse head {h}")
+        assert_close(dq[0, h][rows], rdq[rows], True, f"dq head {h}")
+        assert_close(dk[0, h], rdk, True, f"dk head {h}")
+        assert_close(dv[0, h], rdv, True, f"dv head {h}")
+        if dead:
+            drows = np.concatenate([pm[64 * i:64 * (i + 1)] for i in dead])
+            assert np.all(o[0, h][drows] == 0.0)
+            assert np.all(np.isneginf(lse[0, h][drows]))
+            assert np.all(dq[0, h][drows] == 0.0)
+        _print(f"  head {h}: {len(dead)} blocks without a valid id")

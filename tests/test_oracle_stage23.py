@@ -223,3 +223,41 @@ def test_selection_margins_report_ties():
     _, lists, diag = po.select_blocks(P, 0, 0.8)
     assert list(lists[0]) == [0, 1]
     assert diag["cdf_gap"][0] < 1e-12      # mass lands exactly on tau
+
+
+_MARGIN_ROWS = {"A": [1, 3, 5, 3, 0, 2, 2, 0], "B": [6, 1, 4, 2, 3, 0, 0, 0]}
+
+
+def _frac(text):
+    if text == "inf":
+        return math.inf
+    if "/" in text:
+        a, b = text.split("/")
+        return float(a) / float(b)
+    return float(text)
+
+
+def _read_margin_golden():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "selection_margins.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, ktau, count, sg, cg = (f.strip() for f in line.split("|"))
+        k, tau = ktau.split()
+        rows.append((name, int(k), float(tau), int(count), _frac(sg), _frac(cg)))
+    return rows
+
+
+@pytest.mark.parametrize("name,k,tau,count,set_gap,cdf_gap", _read_margin_golden())
+def test_selection_margins_golden(name, k, tau, count, set_gap, cdf_gap):
+    """Hand-derived decision margins (tests/golden/selection_margins.txt):
+    rows where k decides the count and rows where tau does, with and without
+    a mass gap below the crossing."""
+    p = np.array(_MARGIN_ROWS[name], dtype=float) / 16.0
+    counts, _, diag = po.select_blocks(p[None, :], k, tau)
+    assert counts[0] == count
+    for got, want in ((diag["set_gap"][0], set_gap), (diag["cdf_gap"][0], cdf_gap)):
+        if math.isinf(want):
+            assert math.isinf(got)
+        else:
+            assert got == pytest.approx(want, rel=1e-12, abs=1e-15)
