@@ -23,7 +23,8 @@ from typing import Optional
 
 __all__ = [
     "PrismError", "lib", "LIB_PATH", "PRISM_FP32", "PRISM_BF16",
-    "prism_zone_shapes", "prism_pool_blocks", "prism_select_blocks",
+    "prism_zone_shapes", "prism_zone_shapes_noalloc", "prism_pool_blocks",
+    "prism_select_blocks",
     "prism_sparse_attn_fwd", "prism_sparse_attn_bwd",
     "prism_zone_shapes_workspace_bytes", "prism_sparse_attn_bwd_workspace_bytes",
     "prism_sparse_attn_fwd_workspace_bytes", "prism_shape_table",
@@ -61,6 +62,10 @@ _SIGS = {
                                    _c_int, _c_int, _c_int, _c_int, _c_int,
                                    _c_dbl, _c_int, _c_p, _c_p, _c_p, _c_p,
                                    _c_p, _c_sz, _c_p]),
+    "prism_zone_shapes_noalloc": (_c_int, [_c_p, _c_p, _c_int, _c_int, _c_int,
+                                           _c_int, _c_int, _c_int, _c_int,
+                                           _c_int, _c_int, _c_dbl, _c_int,
+                                           _c_p, _c_p, _c_p, _c_p, _c_p]),
     "prism_pool_blocks": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_int,
                                    _c_int, _c_int, _c_p, _c_p, _c_p, _c_p]),
     "prism_select_blocks": (_c_int, [_c_p, _c_int, _c_int, _c_int, _c_int,
@@ -177,6 +182,14 @@ def prism_zone_shapes(feat, a2v_res, dtype, B, T, H, W, C, zone_t, zone_h,
     return _call("prism_zone_shapes", feat, a2v_res, dtype, B, T, H, W, C,
                  zone_t, zone_h, zone_w, lambda_a2v, fixed_shape, zone_shape,
                  perm, inv_perm, zone_stats, workspace, workspace_bytes, stream)
+
+
+def prism_zone_shapes_noalloc(feat, a2v_res, dtype, B, T, H, W, C, zone_t,
+                              zone_h, zone_w, lambda_a2v, fixed_shape,
+                              zone_shape, perm, inv_perm, zone_stats, stream):
+    return _call("prism_zone_shapes_noalloc", feat, a2v_res, dtype, B, T, H, W,
+                 C, zone_t, zone_h, zone_w, lambda_a2v, fixed_shape,
+                 zone_shape, perm, inv_perm, zone_stats, stream)
 
 
 def prism_pool_blocks(q, k, dtype, perm, B, Hh, N, d, q_mean, k_mean, proxy,

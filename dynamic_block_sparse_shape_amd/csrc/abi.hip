@@ -196,16 +196,19 @@ size_t prism_zone_shapes_workspace_bytes(int B, int T, int H, int W, int C,
   return zone_shapes_ws_bytes(B, g, C);
 }
 
-prism_status prism_zone_shapes(const void* feat, const void* a2v_res,
-                               int dtype, int B, int T, int H, int W, int C,
-                               int zone_t, int zone_h, int zone_w,
-                               double lambda_a2v, int fixed_shape,
-                               int32_t* zone_shape, int32_t* perm,
-                               int32_t* inv_perm, double* zone_stats,
-                               void* workspace, size_t workspace_bytes,
-                               void* stream) {
-  clear_error();
-  ZoneGeom g;
+}  // extern "C"
+
+namespace prism {
+// Every argument check of stage 1 except the workspace's (shared by
+// prism_zone_shapes and prism_zone_shapes_noalloc).
+static prism_status check_zone_shapes(const void* feat, const void* a2v_res,
+                                      int dtype, int B, int T, int H, int W,
+                                      int C, int zone_t, int zone_h,
+                                      int zone_w, double lambda_a2v,
+                                      int fixed_shape, int32_t* zone_shape,
+                                      int32_t* perm, int32_t* inv_perm,
+                                      double* zone_stats, ZoneGeom* gout) {
+  ZoneGeom& g = *gout;
   prism_status st = make_geom(T, H, W, zone_t, zone_h, zone_w, &g);
   if (st != PRISM_OK) return st;
   PRISM_CHECK(B >= 1, PRISM_ERR_INVALID_ARG, "B=%d must be >= 1", B);
@@ -216,7 +219,6 @@ prism_status prism_zone_shapes(const void* feat, const void* a2v_res,
               "zone_shape and perm must not be NULL");
   PRISM_CHECK_ALIGNED(feat, 16);
   PRISM_CHECK_ALIGNED(a2v_res, 16);
-  PRISM_CHECK_ALIGNED(workspace, 16);
   PRISM_CHECK_ALIGNED(zone_stats, 8);
   PRISM_CHECK_ALIGNED(zone_shape, 4);
   PRISM_CHECK_ALIGNED(perm, 4);
@@ -234,6 +236,63 @@ prism_status prism_zone_shapes(const void* feat, const void* a2v_res,
                 PRISM_ERR_INVALID_ARG, "lambda_a2v must be finite and >= 0");
     PRISM_CHECK((long long)B * T * H * W * C < (1LL << 40),
                 PRISM_ERR_UNSUPPORTED, "feature tensor too large");
+  }
+  return PRISM_OK;
+}
+
+// Scratch of prism_zone_shapes_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes its name to
+// a kernel (on the host it is only a stand-in symbol); the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current.
+constexpr size_t kZoneScratchBytes = (size_t)PRISM_ZONE_SHAPES_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char zone_scratch[kZoneScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of the current GPU's copy of zone_scratch.
+static prism_status zone_scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(PRISM_ERR_HIP, "hipGetDevice failed or device id %d above %d",
+                dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(zone_scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PRISM_ERR_HIP, "hipGetSymbolAddress(zone scratch): %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PRISM_OK;
+}
+}  // namespace prism
+
+extern "C" {
+
+prism_status prism_zone_shapes(const void* feat, const void* a2v_res,
+                               int dtype, int B, int T, int H, int W, int C,
+                               int zone_t, int zone_h, int zone_w,
+                               double lambda_a2v, int fixed_shape,
+                               int32_t* zone_shape, int32_t* perm,
+                               int32_t* inv_perm, double* zone_stats,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  clear_error();
+  ZoneGeom g;
+  prism_status st = check_zone_shapes(feat, a2v_res, dtype, B, T, H, W, C,
+                                      zone_t, zone_h, zone_w, lambda_a2v,
+                                      fixed_shape, zone_shape, perm, inv_perm,
+                                      zone_stats, &g);
+  if (st != PRISM_OK) return st;
+  PRISM_CHECK_ALIGNED(workspace, 16);
+  if (fixed_shape < 0) {
     size_t need = zone_shapes_ws_bytes(B, g, C);
     PRISM_CHECK(workspace != nullptr && workspace_bytes >= need,
                 PRISM_ERR_WORKSPACE,
@@ -243,6 +302,37 @@ prism_status prism_zone_shapes(const void* feat, const void* a2v_res,
   return launch_zone_shapes(feat, a2v_res, dtype, B, g, C, lambda_a2v,
                             fixed_shape, zone_shape, perm, inv_perm,
                             zone_stats, workspace, (hipStream_t)stream);
+}
+
+prism_status prism_zone_shapes_noalloc(const void* feat, const void* a2v_res,
+                                       int dtype, int B, int T, int H, int W,
+                                       int C, int zone_t, int zone_h,
+                                       int zone_w, double lambda_a2v,
+                                       int fixed_shape, int32_t* zone_shape,
+                                       int32_t* perm, int32_t* inv_perm,
+                                       double* zone_stats, void* stream) {
+  clear_error();
+  ZoneGeom g;
+  prism_status st = check_zone_shapes(feat, a2v_res, dtype, B, T, H, W, C,
+                                      zone_t, zone_h, zone_w, lambda_a2v,
+                                      fixed_shape, zone_shape, perm, inv_perm,
+                                      zone_stats, &g);
+  if (st != PRISM_OK) return st;
+  void* scratch = nullptr;
+  if (fixed_shape < 0) {
+    const size_t need = zone_shapes_ws_bytes(B, g, C);
+    PRISM_CHECK(need <= kZoneScratchBytes, PRISM_ERR_WORKSPACE,
+                "the call needs %zu bytes of scratch; the allocation-free "
+                "entry point holds %zu (use prism_zone_shapes with a "
+                "workspace, or fewer batch elements per call)",
+                need, kZoneScratchBytes);
+    // every scratch word the kernels read is written earlier in the same
+    // call, so nothing needs clearing
+    if ((st = zone_scratch_ptr(&scratch)) != PRISM_OK) return st;
+  }
+  return launch_zone_shapes(feat, a2v_res, dtype, B, g, C, lambda_a2v,
+                            fixed_shape, zone_shape, perm, inv_perm,
+                            zone_stats, scratch, (hipStream_t)stream);
 }
 
 prism_status prism_pool_blocks(const void* q, const void* k, int dtype,

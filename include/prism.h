@@ -127,6 +127,29 @@ prism_status prism_zone_shapes(const void* feat, const void* a2v_res,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* Allocation-free variant of prism_zone_shapes, for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments
+ * and results as prism_zone_shapes without the workspace: the scratch (per
+ * zone and channel slice partial sums, per-token residual norms) lives in a
+ * device array of PRISM_ZONE_SHAPES_SCRATCH_BYTES inside the library, one
+ * copy per GPU, held until the process ends.  Calls needing more scratch
+ * than that -- prism_zone_shapes_workspace_bytes() above the limit; the 2K
+ * grid with C = 3072 needs about 5.6 MB per batch element -- are rejected
+ * with PRISM_ERR_WORKSPACE before any HIP call.  The array is shared by
+ * every call on a GPU: calls that overlap in time on one GPU (different
+ * streams or host threads) race and must be serialised by the caller.  The
+ * call allocates nothing (no hipMalloc, no hipFree); its first use on a
+ * device looks up that device's copy of the array. */
+#define PRISM_ZONE_SHAPES_SCRATCH_BYTES (32u << 20)
+prism_status prism_zone_shapes_noalloc(const void* feat, const void* a2v_res,
+                                       int dtype, int B, int T, int H, int W,
+                                       int C, int zone_t, int zone_h,
+                                       int zone_w, double lambda_a2v,
+                                       int fixed_shape, int32_t* zone_shape,
+                                       int32_t* perm, int32_t* inv_perm,
+                                       double* zone_stats, void* stream);
+
 /* ---------------------------------------------------------------------
  * Stage 2 -- block mean-pooling and block proxy scores.
  * README "Overview" (block-level features) and the abstract page (block

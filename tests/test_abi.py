@@ -23,7 +23,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     L = P.lib()
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(L, n), n
     # the Python binding carries the same names
@@ -61,6 +61,32 @@ def _expect(status, fn, *args, **kw):
         fn(*args, **kw)
     assert ei.value.status == status, str(ei.value)
     assert P.prism_last_error() != ""
+
+
+def test_zone_shapes_noalloc_rejections():
+    """The allocation-free stage-1 call checks its arguments like
+    prism_zone_shapes and refuses calls whose scratch exceeds the library's
+    fixed array, all before any HIP call."""
+    base = dict(feat=FAKE, a2v_res=FAKE, dtype=1, B=1, T=20, H=90, W=160,
+                C=3072, zone_t=8, zone_h=8, zone_w=8, lambda_a2v=1.0,
+                fixed_shape=-1, zone_shape=FAKE, perm=FAKE, inv_perm=None,
+                zone_stats=None, stream=None)
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return P.prism_zone_shapes_noalloc(*a.values())
+
+    limit = 32 << 20
+    need = P.prism_zone_shapes_workspace_bytes(8, 20, 90, 160, 3072, 8, 8, 8)
+    assert need > limit
+    _expect(4, call, B=8)                         # scratch above the limit
+    _expect(2, call, W=161)                       # N % 64 != 0
+    _expect(1, call, feat=None)
+    _expect(1, call, dtype=7)
+    _expect(1, call, perm=FAKE + 2)               # misaligned
+    assert P.prism_zone_shapes_workspace_bytes(1, 20, 90, 160, 3072, 8, 8,
+                                               8) <= limit
 
 
 def test_zone_shapes_rejections():
