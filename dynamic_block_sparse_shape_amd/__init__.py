@@ -30,6 +30,7 @@ __all__ = [
     "prism_sparse_attn_fwd_workspace_bytes", "prism_shape_table",
     "prism_dropped_terms", "prism_dropped_terms_workspace_bytes",
     "prism_sparse_attn_fwd_corrected",
+    "prism_a2v_bridge", "prism_a2v_bridge_workspace_bytes", "a2v_bridge",
     "prism_last_error", "prism_version", "prism_profile_enable",
     "prism_profile_reset", "prism_profile_count", "prism_profile_name",
     "prism_profile_ms", "kernel_times",
@@ -85,6 +86,11 @@ _SIGS = {
                                                  _c_int, _c_int, _c_int, _c_flt,
                                                  _c_p, _c_p, _c_p, _c_p, _c_p,
                                                  _c_sz, _c_p]),
+    "prism_a2v_bridge_workspace_bytes": (_c_sz, [_c_int] * 6),
+    "prism_a2v_bridge": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                  _c_p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                  _c_int, _c_int, _c_flt, _c_p, _c_p, _c_sz,
+                                  _c_p]),
     "prism_sparse_attn_bwd_workspace_bytes": (_c_sz, [_c_int] * 4),
     "prism_sparse_attn_bwd": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                        _c_int, _c_p, _c_p, _c_p, _c_int,
@@ -231,6 +237,18 @@ def prism_sparse_attn_fwd_corrected(q, k, v, dtype, perm, counts, kv_idx,
     return _call("prism_sparse_attn_fwd_corrected", q, k, v, dtype, perm,
                  counts, kv_idx, capacity, B, Hh, N, d, softmax_scale,
                  drop_lse, drop_v, o, lse, workspace, workspace_bytes, stream)
+
+
+def prism_a2v_bridge_workspace_bytes(B, N, Na, Cv, Ca, heads) -> int:
+    return lib().prism_a2v_bridge_workspace_bytes(B, N, Na, Cv, Ca, heads)
+
+
+def prism_a2v_bridge(x_v, x_a, w_q, w_k, w_v, w_o, pos_v, pos_a, dtype, B, N,
+                     Na, Cv, Ca, heads, rope_base, dh, workspace,
+                     workspace_bytes, stream):
+    return _call("prism_a2v_bridge", x_v, x_a, w_q, w_k, w_v, w_o, pos_v,
+                 pos_a, dtype, B, N, Na, Cv, Ca, heads, rope_base, dh,
+                 workspace, workspace_bytes, stream)
 
 
 def prism_sparse_attn_bwd(q, k, v, o, d_o, lse, dtype, perm, counts, kv_idx,
@@ -418,3 +436,23 @@ def sparse_attn_fwd_corrected(q, k, v, perm, counts, kv_idx, drop_lse, drop_v,
                                     _ptr(lse), _ptr(workspace),
                                     workspace.numel(), _stream(stream))
     return o, lse
+
+
+def a2v_bridge(x_v, x_a, w_q, w_k, w_v, w_o, heads: int, pos_v=None,
+               pos_a=None, rope_base: float = 10000.0, workspace=None,
+               stream=None):
+    """Unscaled a2v bridge residual.  x_v [B, N, Cv], x_a [B, Na, Ca],
+    weights [out, in], all bf16; pos_v [B, N] / pos_a [B, Na] fp32 or None.
+    Returns dh [B, N, Cv] bf16."""
+    torch = _torch()
+    B, N, Cv = x_v.shape
+    _, Na, Ca = x_a.shape
+    dh = torch.empty_like(x_v)
+    if workspace is None:
+        need = prism_a2v_bridge_workspace_bytes(B, N, Na, Cv, Ca, heads)
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_v.device)
+    prism_a2v_bridge(_ptr(x_v), _ptr(x_a), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+                     _ptr(w_o), _ptr(pos_v), _ptr(pos_a), _dtype_code(x_v), B,
+                     N, Na, Cv, Ca, heads, float(rope_base), _ptr(dh),
+                     _ptr(workspace), workspace.numel(), _stream(stream))
+    return dh

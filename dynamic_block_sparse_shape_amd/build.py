@@ -21,7 +21,8 @@ OBJDIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("PRISM_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["abi.hip", "zone_shapes.hip", "pool_proxy.hip", "select.hip",
-           "pairing.hip", "attn_fwd.hip", "attn_bwd.hip", "dropped.hip"]
+           "pairing.hip", "attn_fwd.hip", "attn_bwd.hip", "dropped.hip",
+           "bridge.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

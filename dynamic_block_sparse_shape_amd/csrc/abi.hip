@@ -512,6 +512,69 @@ prism_status prism_sparse_attn_fwd_corrected(
                          (hipStream_t)stream);
 }
 
+static prism_status check_bridge(int B, int N, int Na, int Cv, int Ca,
+                                 int heads) {
+  PRISM_CHECK(B >= 1 && N >= 1 && Na >= 1 && Cv >= 1 && Ca >= 1 && heads >= 1,
+              PRISM_ERR_INVALID_ARG,
+              "sizes must be >= 1 (B=%d N=%d Na=%d Cv=%d Ca=%d heads=%d)", B,
+              N, Na, Cv, Ca, heads);
+  PRISM_CHECK(heads % 2 == 0, PRISM_ERR_UNSUPPORTED,
+              "heads=%d must be even (projection tiles of 256 columns)", heads);
+  PRISM_CHECK(Cv % 256 == 0 && Ca % 64 == 0, PRISM_ERR_UNSUPPORTED,
+              "Cv=%d must be a multiple of 256 and Ca=%d of 64", Cv, Ca);
+  const long long D = 128LL * heads;
+  PRISM_CHECK((long long)B * N * (D > Cv ? D : Cv) * 2 < (1LL << 40) &&
+                  256LL * (D > Cv ? D : Cv) * 2 < (1LL << 31) &&
+                  (long long)B * Na * (Ca > D ? Ca : D) < (1LL << 40) &&
+                  (long long)B * N < (1LL << 31),
+              PRISM_ERR_UNSUPPORTED, "tensors too large");
+  return PRISM_OK;
+}
+
+size_t prism_a2v_bridge_workspace_bytes(int B, int N, int Na, int Cv, int Ca,
+                                        int heads) {
+  if (check_bridge(B, N, Na, Cv, Ca, heads) != PRISM_OK) return 0;
+  return a2v_bridge_ws_bytes(B, N, Na, heads);
+}
+
+prism_status prism_a2v_bridge(const void* x_v, const void* x_a,
+                              const void* w_q, const void* w_k,
+                              const void* w_v, const void* w_o,
+                              const float* pos_v, const float* pos_a,
+                              int dtype, int B, int N, int Na, int Cv, int Ca,
+                              int heads, float rope_base, void* dh,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  clear_error();
+  prism_status st = check_bridge(B, N, Na, Cv, Ca, heads);
+  if (st != PRISM_OK) return st;
+  PRISM_CHECK(dtype == PRISM_BF16, PRISM_ERR_UNSUPPORTED,
+              "the bridge is built for bf16 only (dtype %d)", dtype);
+  PRISM_CHECK(x_v && x_a && w_q && w_k && w_v && w_o && dh,
+              PRISM_ERR_INVALID_ARG, "null pointer argument");
+  PRISM_CHECK((pos_v == nullptr) == (pos_a == nullptr), PRISM_ERR_INVALID_ARG,
+              "give both rotary position arrays or neither");
+  PRISM_CHECK(isfinite(rope_base) && rope_base > 1.f, PRISM_ERR_INVALID_ARG,
+              "rope_base must be finite and > 1");
+  PRISM_CHECK_ALIGNED(x_v, 16);
+  PRISM_CHECK_ALIGNED(x_a, 16);
+  PRISM_CHECK_ALIGNED(w_q, 16);
+  PRISM_CHECK_ALIGNED(w_k, 16);
+  PRISM_CHECK_ALIGNED(w_v, 16);
+  PRISM_CHECK_ALIGNED(w_o, 16);
+  PRISM_CHECK_ALIGNED(dh, 16);
+  PRISM_CHECK_ALIGNED(pos_v, 4);
+  PRISM_CHECK_ALIGNED(pos_a, 4);
+  PRISM_CHECK_ALIGNED(workspace, 16);
+  const size_t need = a2v_bridge_ws_bytes(B, N, Na, heads);
+  PRISM_CHECK(workspace != nullptr && workspace_bytes >= need,
+              PRISM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+              need, workspace ? workspace_bytes : (size_t)0);
+  return launch_a2v_bridge(x_v, x_a, w_q, w_k, w_v, w_o, pos_v, pos_a, B, N,
+                           Na, Cv, Ca, heads, rope_base, dh, workspace,
+                           (hipStream_t)stream);
+}
+
 size_t prism_sparse_attn_bwd_workspace_bytes(int B, int Hh, int N, int d) {
   if (check_heads(B, Hh, N, d) != PRISM_OK) return 0;
   return attn_bwd_ws_bytes(B, Hh, N, d);

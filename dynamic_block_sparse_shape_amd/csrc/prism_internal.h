@@ -120,6 +120,17 @@ prism_status launch_dropped_terms(const double* proxy, const double* q_mean,
                                   float* drop_lse, float* drop_v, void* ws,
                                   hipStream_t stream);
 
+// The a2v bridge residual (bridge.hip): projections on bf16 MFMA GEMMs,
+// cross-attention over the audio tokens; heads of 128.
+size_t a2v_bridge_ws_bytes(int B, int N, int Na, int heads);
+prism_status launch_a2v_bridge(const void* x_v, const void* x_a,
+                               const void* w_q, const void* w_k,
+                               const void* w_v, const void* w_o,
+                               const float* pos_v, const float* pos_a, int B,
+                               int N, int Na, int Cv, int Ca, int heads,
+                               float rope_base, void* dh, void* ws,
+                               hipStream_t stream);
+
 size_t attn_bwd_ws_bytes(int B, int Hh, int N, int d);
 prism_status launch_attn_bwd(const void* q, const void* k, const void* v,
                              const void* o, const void* d_o, const float* lse,

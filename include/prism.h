@@ -306,6 +306,46 @@ prism_status prism_sparse_attn_fwd_corrected(
     const float* drop_lse, const float* drop_v, void* o, float* lse,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------
+ * Producer of stage 1's audio input -- the unscaled a2v bridge residual.
+ * Walk-through sections "a2v / v2a 条件桥" and "一个巧妙的联动：桥接残差反哺稀疏
+ * 注意力": a conditional cross-attention block whose queries are the video
+ * tokens' hidden states (3072 wide in the pages' model) and whose keys and
+ * values come from the audio tokens' hidden states (1536 wide); its output,
+ * before the a2v_scale factor, is the residual whose per-token norm stage 1
+ * reads.  The pages give no formula; this call computes multi-head scaled
+ * dot-product cross-attention with linear projections (no bias, no
+ * normalisation) and heads of 128 (D = 128 * heads):
+ *   q = x_v Wq^T, k = x_a Wk^T, v = x_a Wv^T          (each [.., D])
+ *   optional rotary alignment (both directions of the bridge support one):
+ *     q and k of every head rotated pairwise, (2i, 2i+1) by angle
+ *     pos * rope_base^(-2i / 128), pos the token's time position
+ *   o_h = softmax(q_h k_h^T / sqrt(128)) v_h,  dh = concat_h(o_h) Wo^T.
+ *
+ * x_v   : [B, N, Cv] bf16 video hidden states (raster tokens).
+ * x_a   : [B, Na, Ca] bf16 audio hidden states.
+ * w_q   : [D, Cv], w_k, w_v : [D, Ca], w_o : [Cv, D]; bf16, [out, in].
+ * pos_v : [B, N] fp32 and pos_a : [B, Na] fp32 time positions on one axis
+ *         (e.g. audio steps), or both NULL (no rotation).
+ * dtype : PRISM_BF16 (the only one built; UNSUPPORTED otherwise).
+ * heads : even; Cv a multiple of 256, Ca of 64.
+ * dh    : out [B, N, Cv] bf16 -- the unscaled residual (pass it to
+ *         prism_zone_shapes as a2v_res).
+ * workspace : at least prism_a2v_bridge_workspace_bytes() (the projected
+ *         q -- overwritten by the attention output -- k and v, bf16).
+ * Accumulation is fp32 on the bf16 matrix unit; q, k, v, the attention
+ * output and dh are rounded to bf16. */
+size_t prism_a2v_bridge_workspace_bytes(int B, int N, int Na, int Cv, int Ca,
+                                        int heads);
+prism_status prism_a2v_bridge(const void* x_v, const void* x_a,
+                              const void* w_q, const void* w_k,
+                              const void* w_v, const void* w_o,
+                              const float* pos_v, const float* pos_a,
+                              int dtype, int B, int N, int Na, int Cv, int Ca,
+                              int heads, float rope_base, void* dh,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -5,6 +5,9 @@ only; none of the attention method's arithmetic lives here.
 """
 from .inputs import (  # noqa: F401
     CONFIGS,
+    BridgeInputs,
+    audio_tokens_for,
+    make_bridge_inputs,
     ConfigInputs,
     bf16_bits_to_f32,
     f32_to_bf16_bits,

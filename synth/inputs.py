@@ -346,3 +346,66 @@ def _gen_qk_bumps_sub(cfg, ss_q, ss_k, ss_bumps, full_heads, pool):
 
     list(pool.map(one, range(B * Hh)))
     return q, k
+
+
+# --------------------------------------------------------------------------
+# a2v bridge inputs (the producer of the audio residual)
+# --------------------------------------------------------------------------
+AUDIO_STEPS_PER_S = 44100.0 / 2048.0   # audio tokens per second (~21.5)
+VIDEO_FPS = 16.0                       # frames per second of the decoded video
+VAE_T_STRIDE = 4                       # video frames per latent frame
+
+
+def audio_tokens_for(T: int) -> int:
+    """Audio tokens covering the clip of T latent frames: (T-1)*4+1 video
+    frames at VIDEO_FPS, AUDIO_STEPS_PER_S audio tokens per second."""
+    seconds = (VAE_T_STRIDE * (T - 1) + 1) / VIDEO_FPS
+    return int(np.ceil(seconds * AUDIO_STEPS_PER_S))
+
+
+@dataclass
+class BridgeInputs:
+    x_a: np.ndarray        # [B, Na, Ca] audio hidden states (bf16 bits)
+    w_q: np.ndarray        # [D, Cv]  weights as [out, in] (bf16 bits)
+    w_k: np.ndarray        # [D, Ca]
+    w_v: np.ndarray        # [D, Ca]
+    w_o: np.ndarray        # [Cv, D]
+    pos_v: np.ndarray      # [B, N] fp32 time positions in audio steps
+    pos_a: np.ndarray      # [B, Na] fp32
+    heads: int
+
+
+def make_bridge_inputs(T: int, H: int, W: int, B: int = 1, Cv: int = 3072,
+                       Ca: int = 1536, heads: int = 24, Na: Optional[int] = None,
+                       seed: int = 2000) -> BridgeInputs:
+    """Random-weight inputs of the a2v bridge for a T x H x W video grid.
+
+    Audio hidden states ~ N(0, 1); each weight ~ N(0, 1 / fan_in) (so
+    projections keep unit scale); all stored as bf16.  Time positions on
+    the audio-step axis: a video token of latent frame t sits at the time of
+    video frame 4t, i.e. 4 t / VIDEO_FPS seconds; audio token j at j.  The
+    pages fix the audio rate (44100 / 2048) and the 4x temporal stride, not
+    the video frame rate (16 fps here).  Seed children, in order: audio
+    states, Wq, Wk, Wv, Wo.
+    """
+    if Na is None:
+        Na = audio_tokens_for(T)
+    D = 128 * heads
+    kids = np.random.SeedSequence(seed).spawn(5)
+
+    def normal(i, shape, std):
+        x = _rng(kids[i]).standard_normal(size=shape, dtype=np.float32)
+        x *= np.float32(std)
+        return f32_to_bf16_bits(x)
+
+    x_a = normal(0, (B, Na, Ca), 1.0)
+    w_q = normal(1, (D, Cv), 1.0 / np.sqrt(Cv))
+    w_k = normal(2, (D, Ca), 1.0 / np.sqrt(Ca))
+    w_v = normal(3, (D, Ca), 1.0 / np.sqrt(Ca))
+    w_o = normal(4, (Cv, D), 1.0 / np.sqrt(D))
+    t = np.repeat(np.arange(T, dtype=np.float64), H * W)
+    pv = (VAE_T_STRIDE * t / VIDEO_FPS * AUDIO_STEPS_PER_S).astype(np.float32)
+    pos_v = np.tile(pv, (B, 1))
+    pos_a = np.tile(np.arange(Na, dtype=np.float32), (B, 1))
+    return BridgeInputs(x_a=x_a, w_q=w_q, w_k=w_k, w_v=w_v, w_o=w_o,
+                        pos_v=pos_v, pos_a=pos_a, heads=heads)
