@@ -296,6 +296,133 @@ def bench_dropped_variant(P, args, w, t, dt_code, fwd_plain_ms, stream):
     }
 
 
+# ------------------------------------------- fused routing (timed apart)
+def bench_fused_routing(P, args, w, t, dt_code, cfg, unfused_ms, stream):
+    """prism_route_blocks (pooling, proxy scores and selection without the
+    [B, Hh, Nb, Nb] proxy matrix) on the same inputs and permutation as the
+    steps, timed after them; counts compared with the steps' unfused ones."""
+    import numpy as np
+    import torch
+    B, Hh, N, d, Nb = w["B"], w["Hh"], w["N"], w["d"], w["Nb"]
+    dev = t["q"].device
+    sh = stream.cuda_stream
+    qm = torch.empty((B, Hh, Nb, d), dtype=torch.float64, device=dev)
+    km = torch.empty_like(qm)
+    counts = torch.empty((B, Hh, Nb), dtype=torch.int32, device=dev)
+    kv = torch.empty((B, Hh, Nb, Nb), dtype=torch.int32, device=dev)
+
+    def once():
+        P.prism_route_blocks(t["q"].data_ptr(), t["k"].data_ptr(), dt_code,
+                             t["perm"].data_ptr(), B, Hh, N, d, cfg["top_k"],
+                             cfg["cdf_threshold"], qm.data_ptr(), km.data_ptr(),
+                             counts.data_ptr(), kv.data_ptr(), Nb, sh)
+
+    once()
+    torch.cuda.synchronize()
+    reps = max(1, min(args.steps, 5))
+    P.prism_profile_enable(1)
+    P.prism_profile_reset()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        once()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    kt = P.kernel_times()
+    P.prism_profile_enable(0)
+    per = {}
+    for name, ms in kt:
+        per.setdefault(name, []).append(ms)
+    kernels = {n: {"avg_ms": float(np.mean(v)), "launches": len(v) / reps}
+               for n, v in per.items()}
+    flops = 2 * B * Hh * Nb * Nb * d
+    rr = kernels["route_rows"]["avg_ms"]
+    same = int((counts == t["counts"]).sum().item())
+    return {
+        "ms": ev[0].elapsed_time(ev[1]) / reps,
+        "unfused_ms": unfused_ms,
+        "kernels": kernels,
+        "route_rows_fp64_tflops": flops / (rr * 1e-3) / 1e12,
+        "route_rows_frac_of_fp64_peak": flops / (rr * 1e-3) / 1e12 / PEAK_FP64_TFLOPS,
+        "proxy_matrix_bytes_avoided": 8 * B * Hh * Nb * Nb,
+        "hbm_footprint_bytes": 16 * B * Hh * Nb * d,
+        "unfused_hbm_footprint_bytes": 16 * B * Hh * Nb * d + 8 * B * Hh * Nb * Nb,
+        "rows_with_unfused_count": same,
+        "rows": B * Hh * Nb,
+    }
+
+
+# ------------------------------------------- a2v bridge (timed apart)
+def bench_bridge(P, args, x, w, stream):
+    """prism_a2v_bridge on the workload's video features (its hidden states)
+    and random-weight audio inputs: the producer of stage 1's residual,
+    timed after the steps (it belongs to the bridge layer, not the sparse
+    attention step)."""
+    import numpy as np
+    import torch
+    from synth import make_bridge_inputs
+    cfg = x.cfg
+    T, H, W = cfg["T"], cfg["H"], cfg["W"]
+    B, N, C = w["B"], w["N"], w["C"]
+    heads, Ca = 24, 1536
+    br = make_bridge_inputs(T, H, W, B=B, Cv=C, Ca=Ca, heads=heads, seed=2500)
+    Na = br.x_a.shape[1]
+    dev = torch.device("cuda", 0)
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    xv = x.dev_feat
+    xa, wq, wk, wv, wo, pv, pa = (up(a) for a in (br.x_a, br.w_q, br.w_k, br.w_v,
+                                                  br.w_o, br.pos_v, br.pos_a))
+    dh = torch.empty_like(xv)
+    need = P.prism_a2v_bridge_workspace_bytes(B, N, Na, C, Ca, heads)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    sh = stream.cuda_stream
+
+    def once():
+        P.prism_a2v_bridge(xv.data_ptr(), xa.data_ptr(), wq.data_ptr(),
+                           wk.data_ptr(), wv.data_ptr(), wo.data_ptr(),
+                           pv.data_ptr(), pa.data_ptr(), P.PRISM_BF16, B, N, Na,
+                           C, Ca, heads, 10000.0, dh.data_ptr(), ws.data_ptr(),
+                           need, sh)
+
+    once()
+    torch.cuda.synchronize()
+    reps = max(1, min(args.steps, 5))
+    P.prism_profile_enable(1)
+    P.prism_profile_reset()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        once()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    kt = P.kernel_times()
+    P.prism_profile_enable(0)
+    D = 128 * heads
+    # launch order per call: q, k, v projections, attention, output projection
+    work = [2 * B * N * C * D, 2 * B * Na * Ca * D, 2 * B * Na * Ca * D,
+            4 * B * N * Na * D, 2 * B * N * D * C]
+    names = ["q_proj", "k_proj", "v_proj", "attention", "out_proj"]
+    per = {n: [] for n in names}
+    for i, (_, ms) in enumerate(kt):
+        per[names[i % 5]].append(ms)
+    launches = {}
+    for n, fl in zip(names, work):
+        ms = float(np.mean(per[n]))
+        launches[n] = {"avg_ms": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+                       "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+    total_ms = ev[0].elapsed_time(ev[1]) / reps
+    return {"ms": total_ms, "audio_tokens": Na, "heads": heads,
+            "video_width": C, "audio_width": Ca,
+            "tflops": sum(work) / (total_ms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": sum(work) / (total_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "launches": launches}
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
@@ -521,6 +648,15 @@ def main():
         P, args, w, dict(q=q, k=k, v=v, perm=perm, qm=qm, km=km, proxy=proxy,
                          counts=counts, kv_idx=kv_idx, wsf=wsf, lse=lse),
         dt_code, stage_ms["attn_fwd"], stream)}
+    _log("variant: forward with the stand-in done")
+    out["variants"]["fused_routing"] = bench_fused_routing(
+        P, args, w, dict(q=q, k=k, perm=perm, counts=counts), dt_code, cfg,
+        stage_ms["pool_proxy"] + stage_ms["select"], stream)
+    _log("variant: fused routing done")
+    if dyn and bf16:
+        x.dev_feat = feat
+        out["variants"]["a2v_bridge"] = bench_bridge(P, args, x, w, stream)
+        _log("variant: a2v bridge done")
     if not args.no_cpu_baseline:
         perm_host = perm.cpu().numpy()
         t0 = time.perf_counter()

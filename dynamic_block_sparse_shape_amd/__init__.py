@@ -24,7 +24,7 @@ from typing import Optional
 __all__ = [
     "PrismError", "lib", "LIB_PATH", "PRISM_FP32", "PRISM_BF16",
     "prism_zone_shapes", "prism_zone_shapes_noalloc", "prism_pool_blocks",
-    "prism_select_blocks",
+    "prism_select_blocks", "prism_route_blocks", "route_blocks",
     "prism_sparse_attn_fwd", "prism_sparse_attn_bwd",
     "prism_zone_shapes_workspace_bytes", "prism_sparse_attn_bwd_workspace_bytes",
     "prism_sparse_attn_fwd_workspace_bytes", "prism_shape_table",
@@ -69,6 +69,9 @@ _SIGS = {
                                            _c_p, _c_p, _c_p, _c_p, _c_p]),
     "prism_pool_blocks": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_int,
                                    _c_int, _c_int, _c_p, _c_p, _c_p, _c_p]),
+    "prism_route_blocks": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_dbl, _c_p, _c_p,
+                                    _c_p, _c_p, _c_int, _c_p]),
     "prism_select_blocks": (_c_int, [_c_p, _c_int, _c_int, _c_int, _c_int,
                                      _c_dbl, _c_p, _c_p, _c_int, _c_p]),
     "prism_sparse_attn_fwd_workspace_bytes": (_c_sz, [_c_int] * 4),
@@ -202,6 +205,13 @@ def prism_pool_blocks(q, k, dtype, perm, B, Hh, N, d, q_mean, k_mean, proxy,
                       stream):
     return _call("prism_pool_blocks", q, k, dtype, perm, B, Hh, N, d, q_mean,
                  k_mean, proxy, stream)
+
+
+def prism_route_blocks(q, k, dtype, perm, B, Hh, N, d, top_k, cdf_threshold,
+                       q_mean, k_mean, counts, kv_idx, capacity, stream):
+    return _call("prism_route_blocks", q, k, dtype, perm, B, Hh, N, d, top_k,
+                 cdf_threshold, q_mean, k_mean, counts, kv_idx, capacity,
+                 stream)
 
 
 def prism_select_blocks(proxy, B, Hh, Nb, top_k, cdf_threshold, counts,
@@ -353,6 +363,24 @@ def select_blocks(proxy, top_k: int, cdf_threshold: float = 0.20,
                         float(cdf_threshold), _ptr(counts), _ptr(kv_idx), cap,
                         _stream(stream))
     return counts, kv_idx
+
+
+def route_blocks(q, k, perm, top_k: int, cdf_threshold: float = 0.20,
+                 capacity: Optional[int] = None, stream=None):
+    """Stages 2-3 fused, without the proxy matrix.  q, k: [B, Hh, N, d].
+    Returns (q_mean, k_mean, counts, kv_idx)."""
+    torch = _torch()
+    B, Hh, N, d = q.shape
+    Nb = N // 64
+    cap = Nb if capacity is None else capacity
+    qm = torch.empty((B, Hh, Nb, d), dtype=torch.float64, device=q.device)
+    km = torch.empty_like(qm)
+    counts = torch.empty((B, Hh, Nb), dtype=torch.int32, device=q.device)
+    kv_idx = torch.empty((B, Hh, Nb, cap), dtype=torch.int32, device=q.device)
+    prism_route_blocks(_ptr(q), _ptr(k), _dtype_code(q), _ptr(perm), B, Hh, N,
+                       d, int(top_k), float(cdf_threshold), _ptr(qm), _ptr(km),
+                       _ptr(counts), _ptr(kv_idx), cap, _stream(stream))
+    return qm, km, counts, kv_idx
 
 
 def sparse_attn_fwd(q, k, v, perm, counts, kv_idx,

@@ -22,7 +22,7 @@ ARCH = os.environ.get("PRISM_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["abi.hip", "zone_shapes.hip", "pool_proxy.hip", "select.hip",
            "pairing.hip", "attn_fwd.hip", "attn_bwd.hip", "dropped.hip",
-           "bridge.hip"]
+           "bridge.hip", "route.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -381,6 +381,42 @@ prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
                        capacity, (hipStream_t)stream);
 }
 
+prism_status prism_route_blocks(const void* q, const void* k, int dtype,
+                                const int32_t* perm, int B, int Hh, int N,
+                                int d, int top_k, double cdf_threshold,
+                                double* q_mean, double* k_mean,
+                                int32_t* counts, int32_t* kv_idx, int capacity,
+                                void* stream) {
+  clear_error();
+  prism_status st = check_heads(B, Hh, N, d);
+  if (st != PRISM_OK) return st;
+  PRISM_CHECK(dtype_ok(dtype), PRISM_ERR_INVALID_ARG, "bad dtype %d", dtype);
+  PRISM_CHECK(q && k && perm && q_mean && k_mean && counts && kv_idx,
+              PRISM_ERR_INVALID_ARG, "null pointer argument");
+  PRISM_CHECK_ALIGNED(q, 16);
+  PRISM_CHECK_ALIGNED(k, 16);
+  PRISM_CHECK_ALIGNED(q_mean, 16);
+  PRISM_CHECK_ALIGNED(k_mean, 16);
+  PRISM_CHECK_ALIGNED(perm, 4);
+  PRISM_CHECK_ALIGNED(counts, 4);
+  PRISM_CHECK_ALIGNED(kv_idx, 4);
+  const int Nb = N / PRISM_BLOCK_TOKENS;
+  PRISM_CHECK(Nb <= 8192, PRISM_ERR_UNSUPPORTED, "Nb=%d above 8192", Nb);
+  PRISM_CHECK(top_k >= 0, PRISM_ERR_INVALID_ARG, "top_k=%d must be >= 0",
+              top_k);
+  PRISM_CHECK(cdf_threshold >= 0.0 && cdf_threshold <= 1.0,
+              PRISM_ERR_INVALID_ARG, "cdf_threshold=%g outside [0, 1]",
+              cdf_threshold);
+  PRISM_CHECK(capacity >= Nb, PRISM_ERR_SHAPE, "capacity=%d < Nb=%d",
+              capacity, Nb);
+  hipStream_t s = (hipStream_t)stream;
+  if ((st = launch_pool_means(q, k, dtype, perm, B, Hh, N, d, q_mean, k_mean,
+                              s)) != PRISM_OK)
+    return st;
+  return launch_route_fused(q_mean, k_mean, B, Hh, Nb, d, top_k, cdf_threshold,
+                            counts, kv_idx, capacity, s);
+}
+
 size_t prism_sparse_attn_fwd_workspace_bytes(int B, int Hh, int N, int d) {
   if (check_heads(B, Hh, N, d) != PRISM_OK) return 0;
   return attn_fwd_ws_bytes(B, Hh, N, d);

@@ -219,17 +219,23 @@ prism_status launch_pool(const void* q, const void* k, const int32_t* perm,
 
 }  // namespace
 
+prism_status launch_pool_means(const void* q, const void* k, int dtype,
+                               const int32_t* perm, int B, int Hh, int N,
+                               int d, double* q_mean, double* k_mean,
+                               hipStream_t stream) {
+  if (dtype == PRISM_BF16)
+    return d == 128 ? launch_pool<uint16_t, 128>(q, k, perm, B, Hh, N, q_mean, k_mean, stream)
+                    : launch_pool<uint16_t, 64>(q, k, perm, B, Hh, N, q_mean, k_mean, stream);
+  return d == 128 ? launch_pool<float, 128>(q, k, perm, B, Hh, N, q_mean, k_mean, stream)
+                  : launch_pool<float, 64>(q, k, perm, B, Hh, N, q_mean, k_mean, stream);
+}
+
 prism_status launch_pool_proxy(const void* q, const void* k, int dtype,
                                const int32_t* perm, int B, int Hh, int N,
                                int d, double* q_mean, double* k_mean,
                                double* proxy, hipStream_t stream) {
-  prism_status st;
-  if (dtype == PRISM_BF16)
-    st = d == 128 ? launch_pool<uint16_t, 128>(q, k, perm, B, Hh, N, q_mean, k_mean, stream)
-                  : launch_pool<uint16_t, 64>(q, k, perm, B, Hh, N, q_mean, k_mean, stream);
-  else
-    st = d == 128 ? launch_pool<float, 128>(q, k, perm, B, Hh, N, q_mean, k_mean, stream)
-                  : launch_pool<float, 64>(q, k, perm, B, Hh, N, q_mean, k_mean, stream);
+  prism_status st = launch_pool_means(q, k, dtype, perm, B, Hh, N, d, q_mean,
+                                      k_mean, stream);
   if (st != PRISM_OK) return st;
 
   const int Nb = N / 64;

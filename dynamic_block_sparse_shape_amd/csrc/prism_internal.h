@@ -82,6 +82,18 @@ prism_status launch_pool_proxy(const void* q, const void* k, int dtype,
                                int d, double* q_mean, double* k_mean,
                                double* proxy, hipStream_t stream);
 
+prism_status launch_pool_means(const void* q, const void* k, int dtype,
+                               const int32_t* perm, int B, int Hh, int N,
+                               int d, double* q_mean, double* k_mean,
+                               hipStream_t stream);
+
+// Fused stages 2b-3 (route.hip): proxy scores and selection without the
+// proxy matrix, from the pooled means.
+prism_status launch_route_fused(const double* q_mean, const double* k_mean,
+                                int B, int Hh, int Nb, int d, int top_k,
+                                double tau, int32_t* counts, int32_t* kv_idx,
+                                int capacity, hipStream_t stream);
+
 prism_status launch_select(const double* proxy, int B, int Hh, int Nb,
                            int top_k, double tau, int32_t* counts,
                            int32_t* kv_idx, int capacity, hipStream_t stream);

@@ -189,6 +189,31 @@ prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
                                  int capacity, void* stream);
 
 /* ---------------------------------------------------------------------
+ * Stages 2-3 fused -- routing without the proxy matrix.
+ * The Sol-Attn abstract on the Prism paper page counts computing and
+ * materialising proxy scores as an overhead and thresholds blocks without
+ * materialising the proxy map; the walk-through ("三者如何协同") runs top-k
+ * then the CDF rule in one gating kernel.  This call pools q and k as
+ * prism_pool_blocks does, then computes each query block's proxy row
+ * (softmax over j of <qbar_i, kbar_j> / sqrt(d), fp64) on chip and selects
+ * from it as prism_select_blocks does -- no [B, Hh, Nb, Nb] buffer exists.
+ * Counts and lists equal those of prism_pool_blocks + prism_select_blocks
+ * except where a decision lies within fp64 rounding of a tie (the logits
+ * are accumulated in another order).
+ *
+ * q, k, dtype, perm, B, Hh, N, d : as prism_pool_blocks.
+ * top_k, cdf_threshold : as prism_select_blocks.
+ * q_mean, k_mean : out [B, Hh, Nb, d] fp64 (as prism_pool_blocks).
+ * counts, kv_idx, capacity : out, as prism_select_blocks.
+ * Nb must be at most 8192; d 64 or 128. */
+prism_status prism_route_blocks(const void* q, const void* k, int dtype,
+                                const int32_t* perm, int B, int Hh, int N,
+                                int d, int top_k, double cdf_threshold,
+                                double* q_mean, double* k_mean,
+                                int32_t* counts, int32_t* kv_idx, int capacity,
+                                void* stream);
+
+/* ---------------------------------------------------------------------
  * Stage 4 -- block-sparse attention, forward.
  * Abstract page (sparse computation over the selected KV blocks with online
  * softmax) and README "Overview": for each query block i and each of its 64

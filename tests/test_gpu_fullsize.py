@@ -224,6 +224,7 @@ def _check_routing(x, g, perm, heads=None):
                     bad_kv.update(sel.tolist())
                     bad_kv.update(route["lists"][i].tolist())
         route["bad_rows"], route["bad_kv"] = bad_rows, bad_kv
+        route["decidable"] = ok
         route.pop("proxy")
         routes[h] = route
     return routes
@@ -290,6 +291,36 @@ def _check_backward(x, g, perm, routes, nsample):
                f"{picks} used by {[len(users[j]) for j in picks]} query blocks")
 
 
+def _check_fused_routing(x, g, routes):
+    """prism_route_blocks (no proxy matrix) on the whole workload, against
+    the oracle on every head: counts and lists bit for bit on the rows fp64
+    can decide, a valid selection within one block of the oracle's count
+    elsewhere."""
+    cfg = x.cfg
+    q, k = _dev(x.q), _dev(x.k)
+    t = time.time()
+    qm, km, counts, kv = P.route_blocks(q, k, g["perm"], cfg["top_k"],
+                                        cfg["cdf_threshold"])
+    torch.cuda.synchronize()
+    _print(f"  fused routing in {time.time() - t:.2f} s (first call)")
+    assert torch.equal(qm, g["qm"]) and torch.equal(km, g["km"])
+    counts, kv = counts.cpu().numpy(), kv.cpu().numpy()
+    ucounts = g["counts"].cpu().numpy()
+    same_as_unfused = int((counts == ucounts).sum())
+    for h, route in routes.items():
+        ok = route["decidable"]
+        for i in range(len(ok)):
+            c = counts[0, h, i]
+            if ok[i]:
+                assert c == route["counts"][i], (h, i)
+                assert np.array_equal(kv[0, h, i, :c], route["lists"][i]), (h, i)
+            else:
+                assert np.all(np.diff(kv[0, h, i, :c]) > 0)
+                assert abs(int(c) - int(route["counts"][i])) <= 1
+    _print(f"  fused routing: {len(routes)} heads against the oracle; counts "
+           f"equal to the unfused path on {same_as_unfused} of {ucounts.size} rows")
+
+
 @pytest.mark.parametrize("cid", [1, 2, 3])
 def test_forward_full_size(cid):
     x = _inputs(cid)
@@ -301,6 +332,7 @@ def test_forward_full_size(cid):
     _check_stage1(x, g, ref)
     perm = ref["perm"]
     routes = _check_routing(x, g, perm)
+    _check_fused_routing(x, g, routes)
     heads = [0, x.cfg["Hh"] - 1]
     _check_forward(x, g, perm, {h: routes[h] for h in heads}, nsample=12,
                    bf16=True)
