@@ -24,7 +24,8 @@ from typing import Optional
 __all__ = [
     "PrismError", "lib", "LIB_PATH", "PRISM_FP32", "PRISM_BF16",
     "prism_zone_shapes", "prism_zone_shapes_noalloc", "prism_pool_blocks",
-    "prism_select_blocks", "prism_route_blocks", "route_blocks",
+    "prism_select_blocks", "prism_route_blocks",
+    "prism_route_blocks_workspace_bytes", "route_blocks",
     "prism_sparse_attn_fwd", "prism_sparse_attn_bwd",
     "prism_zone_shapes_workspace_bytes", "prism_sparse_attn_bwd_workspace_bytes",
     "prism_sparse_attn_fwd_workspace_bytes", "prism_shape_table",
@@ -69,9 +70,10 @@ _SIGS = {
                                            _c_p, _c_p, _c_p, _c_p, _c_p]),
     "prism_pool_blocks": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_int,
                                    _c_int, _c_int, _c_p, _c_p, _c_p, _c_p]),
+    "prism_route_blocks_workspace_bytes": (_c_sz, [_c_int] * 4),
     "prism_route_blocks": (_c_int, [_c_p, _c_p, _c_int, _c_p, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_dbl, _c_p, _c_p,
-                                    _c_p, _c_p, _c_int, _c_p]),
+                                    _c_p, _c_p, _c_int, _c_p, _c_sz, _c_p]),
     "prism_select_blocks": (_c_int, [_c_p, _c_int, _c_int, _c_int, _c_int,
                                      _c_dbl, _c_p, _c_p, _c_int, _c_p]),
     "prism_sparse_attn_fwd_workspace_bytes": (_c_sz, [_c_int] * 4),
@@ -207,11 +209,16 @@ def prism_pool_blocks(q, k, dtype, perm, B, Hh, N, d, q_mean, k_mean, proxy,
                  k_mean, proxy, stream)
 
 
+def prism_route_blocks_workspace_bytes(B, Hh, N, d) -> int:
+    return lib().prism_route_blocks_workspace_bytes(B, Hh, N, d)
+
+
 def prism_route_blocks(q, k, dtype, perm, B, Hh, N, d, top_k, cdf_threshold,
-                       q_mean, k_mean, counts, kv_idx, capacity, stream):
+                       q_mean, k_mean, counts, kv_idx, capacity, workspace,
+                       workspace_bytes, stream):
     return _call("prism_route_blocks", q, k, dtype, perm, B, Hh, N, d, top_k,
                  cdf_threshold, q_mean, k_mean, counts, kv_idx, capacity,
-                 stream)
+                 workspace, workspace_bytes, stream)
 
 
 def prism_select_blocks(proxy, B, Hh, Nb, top_k, cdf_threshold, counts,
@@ -377,9 +384,12 @@ def route_blocks(q, k, perm, top_k: int, cdf_threshold: float = 0.20,
     km = torch.empty_like(qm)
     counts = torch.empty((B, Hh, Nb), dtype=torch.int32, device=q.device)
     kv_idx = torch.empty((B, Hh, Nb, cap), dtype=torch.int32, device=q.device)
+    need = prism_route_blocks_workspace_bytes(B, Hh, N, d)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     prism_route_blocks(_ptr(q), _ptr(k), _dtype_code(q), _ptr(perm), B, Hh, N,
                        d, int(top_k), float(cdf_threshold), _ptr(qm), _ptr(km),
-                       _ptr(counts), _ptr(kv_idx), cap, _stream(stream))
+                       _ptr(counts), _ptr(kv_idx), cap, _ptr(ws), need,
+                       _stream(stream))
     return qm, km, counts, kv_idx
 
 

@@ -381,11 +381,17 @@ prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
                        capacity, (hipStream_t)stream);
 }
 
+size_t prism_route_blocks_workspace_bytes(int B, int Hh, int N, int d) {
+  if (check_heads(B, Hh, N, d) != PRISM_OK) return 0;
+  return route_fused_ws_bytes(B, Hh, N / PRISM_BLOCK_TOKENS, d);
+}
+
 prism_status prism_route_blocks(const void* q, const void* k, int dtype,
                                 const int32_t* perm, int B, int Hh, int N,
                                 int d, int top_k, double cdf_threshold,
                                 double* q_mean, double* k_mean,
                                 int32_t* counts, int32_t* kv_idx, int capacity,
+                                void* workspace, size_t workspace_bytes,
                                 void* stream) {
   clear_error();
   prism_status st = check_heads(B, Hh, N, d);
@@ -409,12 +415,17 @@ prism_status prism_route_blocks(const void* q, const void* k, int dtype,
               cdf_threshold);
   PRISM_CHECK(capacity >= Nb, PRISM_ERR_SHAPE, "capacity=%d < Nb=%d",
               capacity, Nb);
+  PRISM_CHECK_ALIGNED(workspace, 16);
+  const size_t need = route_fused_ws_bytes(B, Hh, Nb, d);
+  PRISM_CHECK(workspace != nullptr && workspace_bytes >= need,
+              PRISM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+              need, workspace ? workspace_bytes : (size_t)0);
   hipStream_t s = (hipStream_t)stream;
   if ((st = launch_pool_means(q, k, dtype, perm, B, Hh, N, d, q_mean, k_mean,
                               s)) != PRISM_OK)
     return st;
   return launch_route_fused(q_mean, k_mean, B, Hh, Nb, d, top_k, cdf_threshold,
-                            counts, kv_idx, capacity, s);
+                            counts, kv_idx, capacity, workspace, s);
 }
 
 size_t prism_sparse_attn_fwd_workspace_bytes(int B, int Hh, int N, int d) {

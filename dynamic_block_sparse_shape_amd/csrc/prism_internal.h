@@ -89,10 +89,11 @@ prism_status launch_pool_means(const void* q, const void* k, int dtype,
 
 // Fused stages 2b-3 (route.hip): proxy scores and selection without the
 // proxy matrix, from the pooled means.
+size_t route_fused_ws_bytes(int B, int Hh, int Nb, int d);
 prism_status launch_route_fused(const double* q_mean, const double* k_mean,
                                 int B, int Hh, int Nb, int d, int top_k,
                                 double tau, int32_t* counts, int32_t* kv_idx,
-                                int capacity, hipStream_t stream);
+                                int capacity, void* ws, hipStream_t stream);
 
 prism_status launch_select(const double* proxy, int B, int Hh, int Nb,
                            int top_k, double tau, int32_t* counts,

@@ -4,93 +4,87 @@
 // The Sol-Attn abstract on the Prism paper page names computing and
 // materialising proxy scores as an overhead and thresholds blocks without
 // materialising the proxy map; the walk-through ("三者如何协同") runs top-k
-// then the CDF rule in one gating kernel.  Here one workgroup of 1024
-// threads takes R query blocks of one head:
-//   1. logits z_ij = <qbar_i, kbar_j> / sqrt(d) for its R rows and every
-//      column j, in fp64: thread t owns columns t + 1024 e; kbar is staged
-//      through LDS in 16-deep slices of 1024 columns (128-byte rows, XOR
-//      swizzle), qbar is read with wave-uniform (scalar) loads; R * NPT
-//      accumulators per thread, one fp64 FMA chain each;
-//   2. per row: softmax in fp64 exactly as the stage-2 kernel writes it
-//      (max, exp(z - max), sum, times the reciprocal), and the stage-3
-//      selection (select_core.h) on the probabilities held in registers.
-// kbar of a head (4.6 MB at the 2K grid) is read once per R rows, from L2
-// (the workgroups of an XCD sweep the same columns in the same order); the
-// logits never leave the chip.  Counts and lists equal those of the unfused
-// calls except where a decision lies within fp64 rounding of a tie: the
-// logits are summed in another order than the stage-2 GEMM's.
+// then the CDF rule in one gating kernel.
+//
+//   kbar_pairs   kbar [bh][Nb][d] -> [bh][d/2][Nb][2] (workspace): a
+//                column's d-pair is then one 16-byte load whose neighbours
+//                in the wave are the neighbouring columns (fully coalesced).
+//   route_rows   one workgroup of 1024 threads per R query blocks of a
+//                head (R = 8 up to 5120 blocks, 4 above):
+//     1. logits z_ij = <qbar_i, kbar_j> / sqrt(d) for its R rows and every
+//        column j, in fp64: thread t owns columns t + 1024 e and streams
+//        their kbar pairs straight from memory (L2: the workgroups of an
+//        XCD walk the same head), qbar comes from LDS (broadcast reads);
+//        R * NPT accumulators per thread, one FMA chain each;
+//     2. per row: softmax in fp64 exactly as the stage-2 kernel writes it
+//        (max, exp(z - max), sum, times the reciprocal), and the stage-3
+//        selection (select_core.h) on the probabilities in registers.
+//   kbar of a head (4.6 MB at the 2K grid) is read once per R rows; the
+//   logits never leave the chip.  Counts and lists
+//   equal those of the unfused calls except where a decision lies within
+//   fp64 rounding of a tie (the logits are summed in another order than
+//   the stage-2 GEMM's).
 #include "select_core.h"
 
 namespace prism {
 namespace {
 
 constexpr int kNT = 1024;
-constexpr int kSlice = 16;                     // d per LDS slice (128 B)
+
+__global__ __launch_bounds__(256) void kbar_pairs(const double* __restrict__ km,
+                                                  int Nb, int d,
+                                                  double* __restrict__ kt) {
+  const long long bh = blockIdx.y;
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;   // (j, m)
+  const int half = d / 2;
+  if (idx >= (long long)Nb * half) return;
+  const int j = (int)(idx / half), m = (int)(idx % half);
+  const double2 v = *reinterpret_cast<const double2*>(km + (bh * Nb + j) * d + 2 * m);
+  *reinterpret_cast<double2*>(kt + ((bh * half + m) * Nb + j) * 2) = v;
+}
 
 template <int NPT, int R>
 __global__ __launch_bounds__(kNT, 1) void route_rows(
-    const double* __restrict__ qm, const double* __restrict__ km, int Nb,
+    const double* __restrict__ qm, const double* __restrict__ kt, int Nb,
     int d, double sqrt_d, int top_k, double tau, int32_t* __restrict__ counts,
     int32_t* __restrict__ kv_idx, int capacity) {
-  // phase 1: the kbar slice (1024 rows x 128 B); phase 2: the selection
-  extern __shared__ __align__(16) unsigned char dyn[];
+  __shared__ sel::SelShared<kNT> sh;
   __shared__ double red[kNT / 64];
-  sel::SelShared<kNT>& sh = *reinterpret_cast<sel::SelShared<kNT>*>(dyn);
+  __shared__ __align__(16) double sq[R][128];
   const long long bh = blockIdx.y;
   const int i0 = blockIdx.x * R;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = d / 2;
   const double* Q = qm + bh * Nb * (long long)d;
-  const double* K = km + bh * Nb * (long long)d;
+  const double2* KT = reinterpret_cast<const double2*>(kt) + bh * half * (long long)Nb;
 
   double z[R][NPT];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int e = 0; e < NPT; ++e) z[r][e] = 0.0;
-  // query rows past Nb repeat the last row (never written out)
-  int qrow[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) qrow[r] = min(i0 + r, Nb - 1);
+  // the R query rows in LDS (rows past Nb repeat the last one, never
+  // written out); every lane reads the same address (broadcast)
+  for (int t = tid; t < R * d; t += kNT) {
+    const int r = t / d, c = t % d;
+    sq[r][c] = Q[(long long)min(i0 + r, Nb - 1) * d + c];
+  }
+  __syncthreads();
 
-  // this thread's 16-byte pieces of a slice: column (tid + 1024 i) / 8,
-  // piece tid % 8; stored at the column's 128-byte row, piece slot XORed
-  // with bits 2-4 of the column so that a wave's reads of one piece from
-  // 8 consecutive columns hit 8 different slots
-  const int piece = tid & 7;
 #pragma unroll
   for (int e = 0; e < NPT; ++e) {
-    const int c0 = kNT * e;
-    for (int ds = 0; ds < d; ds += kSlice) {
-      __syncthreads();
+    const int j = tid + kNT * e;
+    if (j < Nb) {
+      const double2* col = KT + j;
+#pragma unroll 4
+      for (int m = 0; m < half; ++m) {
+        const double2 kv = col[(long long)m * Nb];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int cl = (tid + kNT * i) >> 3;
-        const int col = c0 + cl;
-        double2 v = {0.0, 0.0};
-        if (col < Nb)
-          v = *reinterpret_cast<const double2*>(K + (long long)col * d + ds + 2 * piece);
-        *reinterpret_cast<double2*>(dyn + cl * 128 + ((piece ^ ((cl >> 2) & 7)) << 4)) = v;
-      }
-      __syncthreads();
-      const unsigned char* mine = dyn + tid * 128;
-      const int sw = (tid >> 2) & 7;
-      double2 kv[8];
-#pragma unroll
-      for (int p = 0; p < 8; ++p)
-        kv[p] = *reinterpret_cast<const double2*>(mine + ((p ^ sw) << 4));
-      // row by row, so only one row's 16 qbar values (scalar registers)
-      // are live at a time
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const double* qr = Q + (long long)qrow[r] * d + ds;
-        double acc = z[r][e];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          acc = fma(qr[2 * p], kv[p].x, acc);
-          acc = fma(qr[2 * p + 1], kv[p].y, acc);
+        for (int r = 0; r < R; ++r) {
+          const double2 q2 = *reinterpret_cast<const double2*>(&sq[r][2 * m]);
+          z[r][e] = fma(q2.x, kv.x, z[r][e]);
+          z[r][e] = fma(q2.y, kv.y, z[r][e]);
         }
-        z[r][e] = acc;
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -143,34 +137,42 @@ __global__ __launch_bounds__(kNT, 1) void route_rows(
 }
 
 template <int NPT, int R>
-prism_status launch_rows(const double* qm, const double* km, int B, int Hh,
+prism_status launch_rows(const double* qm, const double* kt, int B, int Hh,
                          int Nb, int d, int top_k, double tau, int32_t* counts,
                          int32_t* kv_idx, int capacity, hipStream_t stream) {
-  const size_t lds = sizeof(sel::SelShared<kNT>) > (size_t)kNT * 128
-                         ? sizeof(sel::SelShared<kNT>) : (size_t)kNT * 128;
   const dim3 grid((unsigned)((Nb + R - 1) / R), (unsigned)(B * Hh));
-  PRISM_LAUNCH("route_rows", (route_rows<NPT, R>), grid, dim3(kNT), lds,
-               stream, qm, km, Nb, d, sqrt((double)d), top_k, tau, counts,
-               kv_idx, capacity);
+  PRISM_LAUNCH("route_rows", (route_rows<NPT, R>), grid, dim3(kNT), 0, stream,
+               qm, kt, Nb, d, sqrt((double)d), top_k, tau, counts, kv_idx,
+               capacity);
   return check_launch("route_rows");
 }
 
 }  // namespace
 
+size_t route_fused_ws_bytes(int B, int Hh, int Nb, int d) {
+  return align256((size_t)B * Hh * Nb * d * sizeof(double));
+}
+
 prism_status launch_route_fused(const double* q_mean, const double* k_mean,
                                 int B, int Hh, int Nb, int d, int top_k,
                                 double tau, int32_t* counts, int32_t* kv_idx,
-                                int capacity, hipStream_t stream) {
+                                int capacity, void* ws, hipStream_t stream) {
+  double* kt = static_cast<double*>(ws);
+  const long long pairs = (long long)Nb * (d / 2);
+  PRISM_LAUNCH("kbar_pairs", kbar_pairs,
+               dim3((unsigned)((pairs + 255) / 256), (unsigned)(B * Hh)),
+               dim3(256), 0, stream, k_mean, Nb, d, kt);
+  prism_status st = check_launch("kbar_pairs");
+  if (st != PRISM_OK) return st;
   // R rows per workgroup: as many as the registers hold (R * NPT fp64
-  // accumulators per thread), so kbar is re-read Nb / R times per head
+  // accumulators per thread); kbar is read Nb / R times per head
   const int npt = (Nb + kNT - 1) / kNT;
 #define PRISM_ROUTE(NPT_, R_)                                                  \
-  return launch_rows<NPT_, R_>(q_mean, k_mean, B, Hh, Nb, d, top_k, tau,      \
-                               counts, kv_idx, capacity, stream)
+  return launch_rows<NPT_, R_>(q_mean, kt, B, Hh, Nb, d, top_k, tau, counts,  \
+                               kv_idx, capacity, stream)
   if (npt <= 1) PRISM_ROUTE(1, 8);
   if (npt <= 2) PRISM_ROUTE(2, 8);
   if (npt <= 3) PRISM_ROUTE(3, 8);
-  if (npt <= 4) PRISM_ROUTE(4, 8);
   if (npt <= 5) PRISM_ROUTE(5, 8);
   if (npt <= 6) PRISM_ROUTE(6, 4);
   PRISM_ROUTE(8, 4);

@@ -205,12 +205,16 @@ prism_status prism_select_blocks(const double* proxy, int B, int Hh, int Nb,
  * top_k, cdf_threshold : as prism_select_blocks.
  * q_mean, k_mean : out [B, Hh, Nb, d] fp64 (as prism_pool_blocks).
  * counts, kv_idx, capacity : out, as prism_select_blocks.
+ * workspace : at least prism_route_blocks_workspace_bytes() (the pooled
+ *             keys re-laid out for coalesced column reads: B*Hh*Nb*d fp64).
  * Nb must be at most 8192; d 64 or 128. */
+size_t prism_route_blocks_workspace_bytes(int B, int Hh, int N, int d);
 prism_status prism_route_blocks(const void* q, const void* k, int dtype,
                                 const int32_t* perm, int B, int Hh, int N,
                                 int d, int top_k, double cdf_threshold,
                                 double* q_mean, double* k_mean,
                                 int32_t* counts, int32_t* kv_idx, int capacity,
+                                void* workspace, size_t workspace_bytes,
                                 void* stream);
 
 /* ---------------------------------------------------------------------
