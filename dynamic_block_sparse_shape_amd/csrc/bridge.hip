@@ -36,8 +36,6 @@ using namespace tiles;
 constexpr int kGM = 256;       // tokens per GEMM tile
 constexpr int kGN = 256;       // output features per GEMM tile
 constexpr int kGK = 64;        // k per LDS stage (128-byte rows)
-constexpr int kGThreads = 256;
-constexpr int kGPieces = (kGM + kGN) * (kGK * 2 / 16) / kGThreads;   // 16
 using TK = Tile<64>;           // 128-byte rows, XOR-swizzled 16-byte pieces
 
 // Work item of this workgroup: each XCD (workgroup L runs on XCD L % 8)
@@ -58,19 +56,25 @@ __device__ __forceinline__ bool gemm_item(int TT, int FT, int& tm, int& tf) {
   return true;
 }
 
-__global__ __launch_bounds__(kGThreads, 1) void gemm_nt_bf16(
+// NT: 256 threads (four waves of 128 features x 128 tokens, one wave per
+// SIMD) or 512 threads (eight waves of 128 x 64, two per SIMD).
+template <int NT>
+__global__ __launch_bounds__(NT, 1) void gemm_nt_bf16(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wt, int M,
     int F, int K, uint16_t* __restrict__ C, const float* __restrict__ pos,
     float log2_base) {
   extern __shared__ __align__(16) unsigned char dyn[];
   // stage s: X tile (256 rows) then W tile (256 rows), 128 bytes per row
   constexpr int kStage = (kGM + kGN) * kGK * 2;
+  constexpr int kPieces = (kGM + kGN) * (kGK * 2 / 16) / NT;   // per thread
+  constexpr int TW = NT == 256 ? 4 : 2;       // 32-token tiles per wave
   const int TT = (M + kGM - 1) / kGM, FT = F / kGN;
   int tm, tf;
   if (!gemm_item(TT, FT, tm, tf)) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int c = lane & 31, hf = lane >> 5;
   const int wf = wave & 1, wt = wave >> 1;
+  const int tbase = 32 * TW * wt;             // first token row of the wave
   const int m0 = tm * kGM, f0 = tf * kGN;
   const int rows_x = min(kGM, M - m0);
   // one buffer resource per operand tile: rows past M read as zeros
@@ -80,37 +84,36 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_nt_bf16(
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(Wt + (long long)f0 * K), (short)0, kGN * K * 2,
       0x00020000);
-  // piece i of this thread: row (tid + 256 i) / 8 of the 512 stage rows
+  // piece i of this thread: row (tid + NT i) / 8 of the 512 stage rows
   // (X rows 0..255, then W rows), 16-byte piece tid % 8
   const int piece = tid & 7;
-  uint32_t goff[kGPieces];
-#pragma unroll
-  for (int i = 0; i < kGPieces; ++i) {
-    const int r = ((tid + kGThreads * i) >> 3) & 255;
-    goff[i] = (uint32_t)(r * K * 2 + piece * 16);
-  }
-  u32x4 st[kGPieces];
+  const uint32_t goff0 = (uint32_t)((tid >> 3) * K * 2 + piece * 16);
+  const uint32_t gstep = (uint32_t)((NT >> 3) * K * 2);
+  u32x4 st[kPieces];
   auto load = [&](int kt) __attribute__((always_inline)) {
     const uint32_t kb = (uint32_t)(kt * kGK * 2);
 #pragma unroll
-    for (int i = 0; i < kGPieces; ++i)
+    for (int i = 0; i < kPieces; ++i) {
+      constexpr int half = kPieces / 2;
+      const int ii = i < half ? i : i - half;
       st[i] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     i < kGPieces / 2 ? rx : rw, goff[i] + kb, 0, 0));
+                     i < half ? rx : rw, goff0 + ii * gstep + kb, 0, 0));
+    }
   };
   auto store = [&](unsigned char* s) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kGPieces; ++i) {
-      const int r = (tid + kGThreads * i) >> 3;        // 0..511
+    for (int i = 0; i < kPieces; ++i) {
+      const int r = (tid + NT * i) >> 3;        // 0..511
       *reinterpret_cast<u32x4*>(s + TK::off(r, piece)) = st[i];
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][TW];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+    for (int b = 0; b < TW; ++b) acc[a][b] = f32x16{};
 
   const int KT = K / kGK;
   load(0);
@@ -122,26 +125,27 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_nt_bf16(
     const unsigned char* sw = sx + kGM * kGK * 2;
 #pragma unroll
     for (int ks = 0; ks < kGK / 16; ++ks) {
-      bf16x8 fa[4], fb[4];
+      bf16x8 fa[4], fb[TW];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i)
         fa[i] = lds_row8<64>(sw, 128 * wf + 32 * i + c, 2 * ks + hf);
-        fb[i] = lds_row8<64>(sx, 128 * wt + 32 * i + c, 2 * ks + hf);
-      }
+#pragma unroll
+      for (int i = 0; i < TW; ++i)
+        fb[i] = lds_row8<64>(sx, tbase + 32 * i + c, 2 * ks + hf);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
+        for (int b = 0; b < TW; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
     }
     if (kt + 1 < KT) store(dyn + ((kt + 1) & 1) * kStage);
     __syncthreads();
   }
 
   // acc[a][b] holds C^T: register 4e + g of lane (c, hf) is feature
-  // f0 + 128 wf + 32 a + 8 e + 4 hf + g, token m0 + 128 wt + 32 b + c
+  // f0 + 128 wf + 32 a + 8 e + 4 hf + g, token m0 + tbase + 32 b + c
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int tok = m0 + 128 * wt + 32 * b + c;
+  for (int b = 0; b < TW; ++b) {
+    const int tok = m0 + tbase + 32 * b + c;
     if (tok >= M) continue;
     const float p = pos ? pos[tok] : 0.f;
 #pragma unroll
@@ -311,7 +315,7 @@ prism_status gemm(const uint16_t* X, const uint16_t* Wt, int M, int F, int K,
   const long long TT = (M + kGM - 1) / kGM, FT = F / kGN;
   const unsigned grid = (unsigned)(8 * ((TT * FT + 7) / 8));
   const size_t lds = 2 * (size_t)(kGM + kGN) * kGK * 2;
-  PRISM_LAUNCH("bridge_gemm", gemm_nt_bf16, dim3(grid), dim3(kGThreads), lds,
+  PRISM_LAUNCH("bridge_gemm", gemm_nt_bf16<512>, dim3(grid), dim3(512), lds,
                stream, X, Wt, M, F, K, C, pos, log2_base);
   return check_launch("bridge_gemm");
 }

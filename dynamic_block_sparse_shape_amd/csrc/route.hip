@@ -133,6 +133,7 @@ __global__ __launch_bounds__(kNT, 1) void route_rows(
     sel::select_from_keys<NPT, kNT>(key, Nb, top_k, tau, sh,
                                     kv_idx + row * (long long)capacity,
                                     counts + row);
+    __syncthreads();     // sh is reused by the next row's selection
   }
 }
 

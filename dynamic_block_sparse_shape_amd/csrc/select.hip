@@ -19,12 +19,16 @@ __global__ __launch_bounds__(kThreads, 4) void select_rows(
   const int tid = threadIdx.x;
   const long long row = blockIdx.x;
   const double* prow = proxy + row * Nb;
+  // every load in flight at once: a clamped index instead of a branch per
+  // load (a branch lets the compiler wait for each load before the next)
+  double pv[NPT];
+#pragma unroll
+  for (int e = 0; e < NPT; ++e) pv[e] = prow[min(tid + e * kThreads, Nb - 1)];
   unsigned long long key[NPT];
 #pragma unroll
   for (int e = 0; e < NPT; ++e) {
     const int j = tid + e * kThreads;
-    double p = j < Nb ? prow[j] : 0.0;
-    p = p > 0.0 ? p : 0.0;  // scores are probabilities; clamp -0 / NaN
+    const double p = pv[e] > 0.0 ? pv[e] : 0.0;  // probabilities; clamp -0 / NaN
     key[e] = j < Nb ? (unsigned long long)__double_as_longlong(p) : 0ull;
   }
   select_from_keys<NPT, kThreads>(key, Nb, top_k, tau, sh,

@@ -94,7 +94,8 @@ __device__ __forceinline__ unsigned long long tree_max(const unsigned long long*
 // scores of blocks tid + NT * e (e < NPT) as the bit patterns of
 // non-negative doubles in key[] (0 beyond Nb).  Writes the ascending list
 // to out and the count to *count_out.  Every thread of the workgroup calls
-// it; it starts and ends with a barrier, so calls can follow each other.
+// it.  It reuses sh from its first instruction on: a caller that calls it
+// again (or reads sh) in the same workgroup puts a barrier in between.
 template <int NPT, int NT>
 __device__ __forceinline__ void select_from_keys(
     const unsigned long long (&key)[NPT], int Nb, int top_k, double tau,
@@ -102,7 +103,6 @@ __device__ __forceinline__ void select_from_keys(
   constexpr int kWaves = NT / 64;
   const int tid = threadIdx.x;
   const int wave = tid / 64, lane = tid % 64;
-  __syncthreads();
   double total = 0.0;
   unsigned long long kmax = 0ull;
 #pragma unroll
@@ -120,7 +120,7 @@ __device__ __forceinline__ void select_from_keys(
     sh.wsum[wave] = total;
     sh.wmax[wave] = kmax;
   }
-  if (tid < 256) {
+  if (NT == 256 || tid < 256) {
     sh.bits[tid] = 0u;
     sh.hcnt[0][tid] = 0;
     sh.hmass[0][tid] = 0.0;
@@ -168,7 +168,7 @@ __device__ __forceinline__ void select_from_keys(
       const int hb = pass & 1;
       int* hcnt = sh.hcnt[hb];
       double* hmass = sh.hmass[hb];
-      if (tid < 256) {
+      if (NT == 256 || tid < 256) {
         sh.hcnt[hb ^ 1][tid] = 0;
         sh.hmass[hb ^ 1][tid] = 0.0;
       }
@@ -605,7 +605,6 @@ __device__ __forceinline__ void select_from_keys(
     }
   }
   if (tid == 0) *count_out = c;
-  __syncthreads();
 }
 
 }  // namespace sel
