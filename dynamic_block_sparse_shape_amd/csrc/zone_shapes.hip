@@ -153,13 +153,15 @@ __global__ __launch_bounds__(kThreads) void zone_feat_dev(
   double dT = 0.0, dH = 0.0, dW = 0.0;
   if constexpr (sizeof(E) == 2) {
     // bf16: the squared deviation of a line of L <= 8 values is
-    // q - s^2 / L with s the sum and q the sum of squares.  With 8-bit
-    // significands, s and q are exact in fp64 whenever the line's values lie
-    // within 2^17 of each other in magnitude -- the near-constant lines where
-    // the subtraction cancels -- so the result is then exact up to its final
-    // rounding; a line with a wider spread has a deviation of the order of q
-    // itself.  One LDS read per value and axis, two channels per 32-bit
-    // read.
+    // (L q - s^2) / L with s the sum and q the sum of squares.  With 8-bit
+    // significands, s, q, L q and s^2 are exact in fp64 whenever the line's
+    // values lie within 2^17 of each other in magnitude -- the near-constant
+    // lines where the subtraction cancels -- so each numerator is exact and
+    // rounding enters only where numerators are summed and in one division
+    // per axis (all lines along an axis of a zone share L), for any L (also
+    // where 1 / L is not a power of two); a line with a wider spread has a
+    // deviation of the order of q itself.  One LDS read per value and axis,
+    // two channels per 32-bit read.
     constexpr int CP = kRowBytes / 4;          // channel pairs per slice
     constexpr int G = kThreads / CP;           // line groups
     const int cp = threadIdx.x % CP, grp = threadIdx.x / CP;
@@ -176,8 +178,8 @@ __global__ __launch_bounds__(kThreads) void zone_feat_dev(
         q0 = fma(x0, x0, q0);
         q1 = fma(x1, x1, q1);
       }
-      const double invL = 1.0 / (double)L;
-      return (q0 - s0 * s0 * invL) + (q1 - s1 * s1 * invL);
+      const double Ld = (double)L;
+      return (Ld * q0 - s0 * s0) + (Ld * q1 - s1 * s1);   // L x deviation
     };
     for (int l = grp; l < zb.Lt * zb.Lh; l += G)          // W lines (lt, lh)
       dW += line(l * zb.Lw, 1, zb.Lw);
@@ -185,6 +187,9 @@ __global__ __launch_bounds__(kThreads) void zone_feat_dev(
       dH += line((l / zb.Lw) * zb.Lh * zb.Lw + l % zb.Lw, zb.Lw, zb.Lh);
     for (int l = grp; l < zb.Lh * zb.Lw; l += G)          // T lines (lh, lw)
       dT += line(l, zb.Lh * zb.Lw, zb.Lt);
+    dW /= (double)zb.Lw;
+    dH /= (double)zb.Lh;
+    dT /= (double)zb.Lt;
   } else {
     // fp32: two passes per line (mean, then squared deviations): wider
     // inputs do not have exact squares

@@ -66,6 +66,27 @@ def test_stage1_dynamic(dtype):
     assert len(set(ref["zone_shape"].tolist())) >= 4
 
 
+@pytest.mark.parametrize("grid", [(16, 12, 30), (16, 11, 32)])
+def test_stage1_dynamic_odd_remainders(grid):
+    """bf16 zone statistics on zones whose remainder extent is 6 (W = 30)
+    or 3 (H = 11): line lengths whose reciprocal is not a power of two."""
+    cfg = dict(SMALL_DYN)
+    T, H, W = grid
+    cfg.update(T=T, H=H, W=W, C=256, name="odd_remainders")
+    x = make_inputs(cfg)
+    _print("stage1 odd remainders", grid)
+    zs, perm, _, stats = P.zone_shapes(to_dev(x.feat), to_dev(x.a2v), T, H, W)
+    torch.cuda.synchronize()
+    ref = po.zone_shapes(widen(x.feat[0]), widen(x.a2v[0]), T, H, W)
+    assert sorted(set(e for _, ext in ref["zones"] for e in ext)) != [8]
+    np.testing.assert_allclose(stats[0].cpu().numpy(), ref["stats"], rtol=1e-11,
+                               atol=1e-14)
+    ok = ref["margin"] > po.REL_MARGIN_FLAG
+    assert ok.all(), ref["margin"].min()
+    assert np.array_equal(zs[0].cpu().numpy(), ref["zone_shape"])
+    assert np.array_equal(perm[0].cpu().numpy(), ref["perm"])
+
+
 def test_stage1_without_audio_and_lambda():
     cfg = dict(SMALL_DYN)
     x = make_inputs(cfg)
