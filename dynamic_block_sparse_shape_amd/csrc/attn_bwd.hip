@@ -366,8 +366,8 @@ __global__ __launch_bounds__(512, 2) void dq_bf16(
   const int Nb = N / 64;
   extern __shared__ __align__(16) unsigned char dyn[];
   unsigned char* smem = dyn;                    // two (K, V) buffers
-  uint32_t* ulist = reinterpret_cast<uint32_t*>(dyn + 4 * TL::kBytes);
-  uint32_t* bits = ulist + Nb;
+  uint16_t* ulist = reinterpret_cast<uint16_t*>(dyn + 4 * TL::kBytes);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ulist + ((Nb + 1) & ~1));
   __shared__ int s_cnt[8];
 
   long long bh;
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(512, 2) void dq_bf16(
   }
   const float lse2 = lse[head + qrow] * kLog2e;
   const float dlt = delta[head + qrow];
-  const uint32_t mflag = 1u << (16 + half);
+  const uint32_t mflag = 1u << (13 + half);
   f32x16 dqa[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) dqa[t] = f32x16{};
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(512, 2) void dq_bf16(
   // the prologue's loads, and the loop runs no step (dq = 0)
   const int last = max(ucnt - 1, 0);
   auto uid = [&](int t) __attribute__((always_inline)) -> int {
-    return (int)(ulist[min(t, last)] & 0xffffu);
+    return (int)(ulist[min(t, last)] & 0x1fffu);
   };
   int j_n = 0;
   {
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(512, 2) void dq_bf16(
     stage_load<D, 512>(VS_, rv, offs_n);                                    \
     pin_order();                                                            \
     j_n = uid(tt + 5);                                                      \
-    const uint32_t e = __builtin_amdgcn_readfirstlane(ulist[tt]);           \
+    const uint32_t e = __builtin_amdgcn_readfirstlane((uint32_t)ulist[tt]); \
     if (e & mflag)                                                          \
       compute_block(smem + (BUF_) * 2 * TL::kBytes,                         \
                     smem + (BUF_) * 2 * TL::kBytes + TL::kBytes);           \
@@ -666,7 +666,7 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
                  (const uint16_t*)d_o, lse, delta, perm, bits, words, kpairs, Hh, N,
                  heads, scale, dk, dv);
     if ((st = check_launch("dkdv_bf16")) != PRISM_OK) return st;
-    const size_t dyn_q = 4 * tiles::Tile<D>::kBytes + 4 * (size_t)Nb +
+    const size_t dyn_q = 4 * tiles::Tile<D>::kBytes + 2 * (size_t)((Nb + 1) & ~1) +
                          8 * (size_t)((Nb + 31) / 32);
     PRISM_LAUNCH("dq_bf16", dq_bf16<D>, gp, dim3(512), dyn_q, stream, (const uint16_t*)q,
                  (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)d_o,

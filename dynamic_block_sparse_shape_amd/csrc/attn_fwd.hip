@@ -24,13 +24,18 @@ namespace {
 // lists are merged into one ascending union in LDS; each K/V block of the
 // union is gathered from HBM once and serves both query blocks, so the
 // gather traffic drops to the union's share.  Waves 0-3 own the pair's
-// first query block and waves 4-7 its second; within a half, wave (qh, kh) computes queries 32*qh .. +31 against KV rows
-// 32*kh .. +31 of every block, so each 32x32 MFMA tile is reused over a
-// 128-deep (S) or 32-deep (P*V) contraction.  A half skips the union blocks
-// its own list does not hold.  The two kh waves of a query half keep
-// separate online-softmax states, merged once at the end (exactly as a
-// split over KV).  K and V stay row-major in LDS; V^T fragments come from
-// ds_read_b64_tr_b16.  Blocks are staged two ahead through registers.
+// first query block and waves 4-7 its second; within a half, wave (qh, kh)
+// computes queries 32*qh .. +31 against KV rows 32*kh .. +31 of every
+// block, so each 32x32 MFMA tile is reused over a 128-deep (S) or 32-deep
+// (P*V) contraction.  A half skips the union blocks its own list does not
+// hold.  The two kh waves of a query half keep separate online-softmax
+// states, merged once at the end (exactly as a split over KV).  K and V stay
+// row-major in LDS; V^T fragments come from ds_read_b64_tr_b16.
+//
+// The union is walked two entries per step: LDS holds two sets of two K/V
+// slots, one set being computed while the next two entries are copied into
+// the other straight from HBM (buffer loads into LDS, no staging registers;
+// one barrier per two blocks).
 template <int D>
 __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -45,15 +50,18 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
   using SH = Share<D, 512>;
   constexpr int KS = D / 16;     // k-steps of S^T = K Q^T
   constexpr int DT = D / 32;     // 32-row d tiles of O^T
+  constexpr int KP = SH::kPerThread;
   const int Nb = N / 64;
-  // two LDS buffers (K and V of one block each): block t+1 is published into
-  // one while block t is read from the other -- one barrier per block.  Then
-  // the union list (one entry per block: id | in-first << 16 |
-  // in-second << 17) and the two membership bitmaps.
+  // LDS: two sets of two K/V slots (slot u of a set: K, then V of one
+  // block, at u * 2 tiles), as two separate arrays so that the compiler sees
+  // that reads of one set never wait for copies into the other; the union
+  // list in dynamic LDS.  The union's membership bitmaps live in set 0 while
+  // the list is built (before any tile is copied).
+  __shared__ __align__(16) unsigned char set0[4 * TL::kBytes];
+  __shared__ __align__(16) unsigned char set1[4 * TL::kBytes];
   extern __shared__ __align__(16) unsigned char dyn[];
-  unsigned char* smem = dyn;
-  uint32_t* ulist = reinterpret_cast<uint32_t*>(dyn + 4 * TL::kBytes);
-  uint32_t* bits = ulist + Nb;
+  uint16_t* ulist = reinterpret_cast<uint16_t*>(dyn);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(set0);
   __shared__ float sm_m[2][2][32], sm_l[2][2][32];
   __shared__ int s_cnt[8];
 
@@ -87,7 +95,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
   for (int ks = 0; ks < KS; ++ks)
     qreg[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(
         q + (head + qrow) * D + 16 * ks + 8 * hf));
-  const uint32_t mflag = 1u << (16 + half);
+  const uint32_t mflag = 1u << (13 + half);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 oacc[DT];
@@ -95,96 +103,71 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
   for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
   const int krow = 32 * kh + slot_of(c);   // K row feeding this lane's M-row
 
-  Stage<D, 512> kA, vA, kB, vB;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(k, head, N);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(v, head, N);
-  uint32_t offs_n[SH::kPerThread];
+  uint32_t offA[KP], offB[KP];
   // an empty union leaves ulist[0] = block 0 (pair_union), a safe id for
   // the prologue's loads; the loop then runs no step
   const int last = max(ucnt - 1, 0);
   auto uid = [&](int t) __attribute__((always_inline)) -> int {
-    return (int)(ulist[min(t, last)] & 0xffffu);
+    return (int)(ulist[min(t, last)] & 0x1fffu);
   };
-  int j_n = 0;
-  // prologue: block 0 published to buffer 0, block 1 staged, block 2 in
-  // flight, offsets of block 3, id of block 4.  Past the end of the list the
-  // last block is re-fetched, so the loop body has no branches around the
-  // loads and the compiler's wait counters stay exact.
+  auto slot = [&](int set, int u) __attribute__((always_inline)) {
+    return (set ? set1 : set0) + u * 2 * TL::kBytes;
+  };
+  // prologue: entries 0, 1 copied into set 0, offsets of entries 2, 3.
+  // Past the end of the list the last block is re-fetched, so the loop body
+  // has no branches around the loads and the wait counters stay exact.
   {
-    uint32_t o0[SH::kPerThread];
-    stage_offsets<D, 512>(o0, pb, uid(0), tid);
-    stage_load<D, 512>(kA, rk, o0);
-    stage_load<D, 512>(vA, rv, o0);
-    stage_offsets<D, 512>(o0, pb, uid(1), tid);
-    stage_load<D, 512>(kB, rk, o0);
-    stage_load<D, 512>(vB, rv, o0);
-    stage_store<D, 512>(kA, smem, tid);
-    stage_store<D, 512>(vA, smem + TL::kBytes, tid);
-    stage_offsets<D, 512>(o0, pb, uid(2), tid);
-    stage_load<D, 512>(kA, rk, o0);
-    stage_load<D, 512>(vA, rv, o0);
-    stage_offsets<D, 512>(offs_n, pb, uid(3), tid);
-    j_n = uid(4);
+    int rows[KP];
+    stage_rows<D, 512>(rows, pb, uid(0), tid);
+    dma_offsets<D, 512>(offA, rows, tid);
+    stage_rows<D, 512>(rows, pb, uid(1), tid);
+    dma_offsets<D, 512>(offB, rows, tid);
+    stage_dma<D, 512>(slot(0, 0), rk, offA, tid);
+    stage_dma<D, 512>(slot(0, 0) + TL::kBytes, rv, offA, tid);
+    stage_dma<D, 512>(slot(0, 1), rk, offB, tid);
+    stage_dma<D, 512>(slot(0, 1) + TL::kBytes, rv, offB, tid);
+    stage_rows<D, 512>(rows, pb, uid(2), tid);
+    dma_offsets<D, 512>(offA, rows, tid);
+    stage_rows<D, 512>(rows, pb, uid(3), tid);
+    dma_offsets<D, 512>(offB, rows, tid);
   }
 
-// One union block t (in buffer t % 2): publish staged block t+1 into the
-// other buffer, load the rows of block t+4, refill the stage with block t+3,
-// compute block t if this half's list holds it, then turn the rows into
-// offsets.
-#define PRISM_FWD_STEP(T_, BUF_, KS_, VS_)                                  \
-  {                                                                         \
-    const int tt = (T_);                                                    \
-    __syncthreads();                                                        \
-    stage_store<D, 512>(KS_, smem + (1 - (BUF_)) * 2 * TL::kBytes, tid);    \
-    stage_store<D, 512>(VS_, smem + (1 - (BUF_)) * 2 * TL::kBytes +         \
-                                 TL::kBytes, tid);                          \
-    int rows_n[SH::kPerThread];                                             \
-    stage_rows<D, 512>(rows_n, pb, j_n, tid);                               \
-    pin_order();                                                            \
-    stage_load<D, 512>(KS_, rk, offs_n);                                    \
-    stage_load<D, 512>(VS_, rv, offs_n);                                    \
-    pin_order();                                                            \
-    j_n = uid(tt + 5);                                                      \
-    const uint32_t e = __builtin_amdgcn_readfirstlane(ulist[tt]);           \
-    if (e & mflag)                                                          \
-      compute_block(smem + (BUF_) * 2 * TL::kBytes,                         \
-                    smem + (BUF_) * 2 * TL::kBytes + TL::kBytes);           \
-    rows_to_offsets<D, 512>(offs_n, rows_n, tid);                           \
-  }
-
-  auto compute_block = [&](const unsigned char* sk, const unsigned char* sv)
-                           __attribute__((always_inline)) {
-    // S^T (32 kv x 32 q) = K_half Q_half^T
+  // S^T (32 kv x 32 q) = K_half Q_half^T of the block in slot sk
+  auto scores = [&](const unsigned char* sk) __attribute__((always_inline)) {
     f32x16 s = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       s = mfma32(lds_row8<D>(sk, krow, 2 * ks + hf), qreg[ks], s);
-    // online softmax in the log2 domain (scale > 0, so the max of the raw
-    // scores is the max of the scaled ones).  The exponent reference m_run
-    // only moves when a block's max exceeds it by more than 8: until then
-    // the probabilities stay <= 2^8 (exact range in fp32 and bf16) and the
-    // accumulator needs no rescale.
+    return s;
+  };
+  // Online softmax in the log2 domain (scale > 0, so the max of the raw
+  // scores is the max of the scaled ones).  The exponent reference only
+  // moves when a block's max exceeds it by more than 8: until then the
+  // probabilities stay <= 2^8 (exact range in fp32 and bf16) and the
+  // accumulator needs no rescale.  Returns the new reference.
+  auto block_max = [&](const f32x16& s, float m_ref) __attribute__((always_inline)) {
     float mx = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
     mx = xor32_max(mx) * scale_log2;
-    const float m_new = mx > m_run + 8.f ? mx : m_run;
-    const float alpha = exp2_fast(m_run - m_new);
+    return mx > m_ref + 8.f ? mx : m_ref;
+  };
+  // probabilities 2^(s scale - m) in place; returns their sum over the lane
+  // pair (one query's 32 keys)
+  auto probs = [&](f32x16& s, float m) __attribute__((always_inline)) {
     float rs = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[r] = exp2_fast(fmaf(s[r], scale_log2, -m_new));
+      s[r] = exp2_fast(fmaf(s[r], scale_log2, -m));
       rs += s[r];
     }
-    rs = xor32_sum(rs);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {      // the reference moved for some query
-#pragma unroll
-      for (int t2 = 0; t2 < DT; ++t2) oacc[t2] *= alpha;
-    }
-    const bf16x8 p0 = pack8(s, 0), p1 = pack8(s, 1);
-    // O^T (d x 32 q) += V_half^T P^T
+    return xor32_sum(rs);
+  };
+  // O^T (d x 32 q) += V_half^T P^T of the block whose V tile is sv
+  auto pv = [&](const unsigned char* sv, const f32x16& p) __attribute__((always_inline)) {
+    const bf16x8 p0 = pack8(p, 0), p1 = pack8(p, 1);
 #pragma unroll
     for (int mt = 0; mt < DT; ++mt) {
       const int d0 = 32 * mt + 16 * (grp & 1);
@@ -193,21 +176,66 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
       oacc[mt] = mfma32(lds_tr8<D>(sv, r0 + 16, d0, j16), p1, oacc[mt]);
     }
   };
+  auto rescale = [&](float f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t2 = 0; t2 < DT; ++t2) oacc[t2] *= f;
+  };
 
-  // stage B holds block t+1 at even t, stage A at odd t
-  int t = 0;
-  for (; t + 1 < ucnt; t += 2) {
-    PRISM_FWD_STEP(t, 0, kB, vB)
-    PRISM_FWD_STEP(t + 1, 1, kA, vA)
+  auto compute_one = [&](const unsigned char* sk) __attribute__((always_inline)) {
+    f32x16 s = scores(sk);
+    const float m_new = block_max(s, m_run);
+    const float alpha = exp2_fast(m_run - m_new);
+    const float rs = probs(s, m_new);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) rescale(alpha);   // the reference moved for some query
+    pv(sk + TL::kBytes, s);
+  };
+// One step over union entries 2 ss, 2 ss + 1 (in set SET_): once every
+// wave's copies into that set have landed, start copying entries 2 ss + 2,
+// + 3 into the other set, load the rows of entries 2 ss + 4, + 5 (issued
+// first: the wait for them then leaves the copies in flight), compute this
+// half's blocks of the step, then turn the rows into offsets.
+#define PRISM_FWD_STEP(SS_, SET_)                                           \
+  {                                                                         \
+    const int e0i = 2 * (SS_);                                              \
+    wait_loads();                                                           \
+    __syncthreads();                                                        \
+    int rowsA[KP], rowsB[KP];                                               \
+    stage_rows<D, 512>(rowsA, pb, uid(e0i + 4), tid);                       \
+    stage_rows<D, 512>(rowsB, pb, uid(e0i + 5), tid);                       \
+    pin_order();                                                            \
+    stage_dma<D, 512>(slot(1 - (SET_), 0), rk, offA, tid);                  \
+    stage_dma<D, 512>(slot(1 - (SET_), 0) + TL::kBytes, rv, offA, tid);     \
+    stage_dma<D, 512>(slot(1 - (SET_), 1), rk, offB, tid);                  \
+    stage_dma<D, 512>(slot(1 - (SET_), 1) + TL::kBytes, rv, offB, tid);     \
+    pin_order();                                                            \
+    const uint32_t ea = __builtin_amdgcn_readfirstlane((uint32_t)ulist[e0i]); \
+    const uint32_t eb = e0i + 1 < ucnt                                      \
+        ? __builtin_amdgcn_readfirstlane((uint32_t)ulist[e0i + 1]) : 0u;    \
+    const bool ha = (ea & mflag) != 0, hb = (eb & mflag) != 0;             \
+    if (ha) compute_one(slot((SET_), 0));                                   \
+    if (hb) compute_one(slot((SET_), 1));                                   \
+    dma_offsets<D, 512>(offA, rowsA, tid);                                  \
+    dma_offsets<D, 512>(offB, rowsB, tid);                                  \
   }
-  if (t < ucnt) PRISM_FWD_STEP(t, 0, kB, vB)
+
+  // set 0 at even steps, set 1 at odd ones
+  const int nss = (ucnt + 1) / 2;
+  int ss = 0;
+  for (; ss + 1 < nss; ss += 2) {
+    PRISM_FWD_STEP(ss, 0)
+    PRISM_FWD_STEP(ss + 1, 1)
+  }
+  if (ss < nss) PRISM_FWD_STEP(ss, 0)
 #undef PRISM_FWD_STEP
 
   // merge the two KV halves of each query half: waves kh = 1 hand over
   // (m, l, O) through LDS (2 waves x 64 lanes x D/2 floats = 2 * kBytes per
-  // query block)
+  // query block).  The copies issued past the end of the list land first.
+  wait_loads();
   __syncthreads();
-  float* xo = reinterpret_cast<float*>(smem + half * 2 * TL::kBytes);
+  float* xo = reinterpret_cast<float*>(set0 + half * 2 * TL::kBytes);
   if (kh == 1) {
     if (hf == 0) {
       sm_m[half][qh][c] = m_run;
@@ -368,15 +396,15 @@ prism_status launch_attn_fwd(const void* q, const void* k, const void* v,
     if ((st = launch_block_pairs(rowbits, B, Hh, Nb, pws, pairs, stream)) != PRISM_OK)
       return st;
     const dim3 g1(tiles::xcd_grid((Nb + 1) / 2, total));
-    const size_t words = (size_t)(Nb + 31) / 32;
     if (d == 128) {
-      const size_t dyn = 4 * tiles::Tile<128>::kBytes + 4 * (size_t)Nb + 8 * words;
+      // the 16-bit union list (the tiles are static LDS)
+      const size_t dyn = 2 * (size_t)Nb;
       PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<128>, g1, dim3(512), dyn, stream,
                    (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                    perm, counts, kv_idx, capacity, pairs, Hh, N, total, sl2,
                    drop_lse, drop_v, (uint16_t*)o, lse);
     } else {
-      const size_t dyn = 4 * tiles::Tile<64>::kBytes + 4 * (size_t)Nb + 8 * words;
+      const size_t dyn = 2 * (size_t)Nb;
       PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<64>, g1, dim3(512), dyn, stream,
                    (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                    perm, counts, kv_idx, capacity, pairs, Hh, N, total, sl2,

@@ -260,6 +260,44 @@ __device__ __forceinline__ void stage_store(const Stage<D, NT>& s,
         s.v[t];
 }
 
+// Global -> LDS copy of one 64-row tile that bypasses registers
+// (buffer_load_dwordx4 ... lds, gfx950).  One such load fills 1 KiB of LDS
+// from a wave, lane l at byte 16 l, so each lane fetches the piece that the
+// tile's swizzle places there: thread tid covers rows Share::row_of(tid, t)
+// (the rows stage_rows reads) at LDS piece tid % kPieces.  dma_offsets turns
+// those rows into the byte offsets of the pieces to fetch; stage_dma issues
+// the loads.  They complete asynchronously and count in vmcnt: wait for
+// them (vmcnt(0)) before the barrier that publishes the tile, and before
+// the tile area is reused.
+template <int D, int NT = 256>
+__device__ __forceinline__ void dma_offsets(uint32_t* offs, const int* rows,
+                                            int tid) {
+  const int pos = Share<D, NT>::piece_of(tid);
+#pragma unroll
+  for (int t = 0; t < Share<D, NT>::kPerThread; ++t) {
+    const int piece = pos ^ Tile<D>::swz(Share<D, NT>::row_of(tid, t));
+    offs[t] = (uint32_t)rows[t] * (uint32_t)(D * 2) + 16u * (uint32_t)piece;
+  }
+}
+
+template <int D, int NT = 256>
+__device__ __forceinline__ void stage_dma(unsigned char* tile,
+                                          __amdgpu_buffer_rsrc_t r,
+                                          const uint32_t* offs, int tid) {
+  const int wave0 = tid & ~63;
+#pragma unroll
+  for (int t = 0; t < Share<D, NT>::kPerThread; ++t) {
+    unsigned char* dst = tile + Share<D, NT>::row_of(wave0, t) * Tile<D>::kRowBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)dst, 16, offs[t], 0, 0, 0);
+  }
+}
+
+// Wait until every global load of this wave has landed (registers or LDS).
+__device__ __forceinline__ void wait_loads() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // Two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t cvt2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
@@ -294,9 +332,9 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int s) {
 }
 
 // Ascending union of two blocks' KV lists, built by a 512-thread workgroup.
-// Each entry is id | (in list 0) << 16 | (in list 1) << 17.  bits holds
-// 2 * ceil(Nb / 32) words and ulist Nb entries (LDS); s_cnt 8 ints.
-// Nb <= 8192.  Counts are clamped to [0, Nb], ids outside [0, Nb) are
+// Each 16-bit entry is id | (in list 0) << 13 | (in list 1) << 14 (ids
+// fit 13 bits: Nb <= 8192).  bits holds 2 * ceil(Nb / 32) words and ulist
+// Nb entries (LDS); s_cnt 8 ints.  Counts are clamped to [0, Nb], ids outside [0, Nb) are
 // skipped and duplicates merge, so any list gives a valid union.  Returns
 // the union size; when it is 0, ulist[0] holds block 0 with no membership
 // bits (a safe id for the gather prologue).  Ends with a barrier.
@@ -304,7 +342,7 @@ __device__ __forceinline__ int pair_union(const int32_t* __restrict__ lst0,
                                           int cnt0,
                                           const int32_t* __restrict__ lst1,
                                           int cnt1, int Nb, uint32_t* bits,
-                                          uint32_t* ulist, int* s_cnt, int tid) {
+                                          uint16_t* ulist, int* s_cnt, int tid) {
   const int words = (Nb + 31) / 32;
   const int wave = tid >> 6, lane = tid & 63;
   for (int w = tid; w < 2 * words; w += 512) bits[w] = 0u;
@@ -343,11 +381,11 @@ __device__ __forceinline__ int pair_union(const int32_t* __restrict__ lst0,
   }
   while (wu) {
     const int bit = __ffs(wu) - 1;
-    ulist[pos++] = (uint32_t)(tid * 32 + bit) | (((wa >> bit) & 1u) << 16) |
-                   (((wb >> bit) & 1u) << 17);
+    ulist[pos++] = (uint16_t)((tid * 32 + bit) | (((wa >> bit) & 1u) << 13) |
+                              (((wb >> bit) & 1u) << 14));
     wu &= wu - 1u;
   }
-  if (ucnt == 0 && tid == 0) ulist[0] = 0u;
+  if (ucnt == 0 && tid == 0) ulist[0] = 0;
   __syncthreads();
   return ucnt;
 }
