@@ -19,25 +19,25 @@
 namespace prism {
 namespace {
 
-// One workgroup (8 waves) per pair of query blocks (pairs[p]: neighbours in
-// the permuted order whose lists overlap most, see pairing.hip).  The two
-// lists are merged into one ascending union in LDS; each K/V block of the
-// union is gathered from HBM once and serves both query blocks, so the
-// gather traffic drops to the union's share.  Waves 0-3 own the pair's
-// first query block and waves 4-7 its second; within a half, wave (qh, kh)
-// computes queries 32*qh .. +31 against KV rows 32*kh .. +31 of every
-// block, so each 32x32 MFMA tile is reused over a 128-deep (S) or 32-deep
-// (P*V) contraction.  A half skips the union blocks its own list does not
-// hold.  The two kh waves of a query half keep separate online-softmax
-// states, merged once at the end (exactly as a split over KV).  K and V stay
-// row-major in LDS; V^T fragments come from ds_read_b64_tr_b16.
-//
-// The union is walked two entries per step: LDS holds two sets of two K/V
-// slots, one set being computed while the next two entries are copied into
-// the other straight from HBM (buffer loads into LDS, no staging registers;
-// one barrier per two blocks).
+// One workgroup of 4 waves per pair of query blocks (pairs[p]: neighbours
+// in the permuted order whose lists overlap most, see pairing.hip), two
+// workgroups per CU.  The two lists are merged into one ascending union in
+// LDS; each K/V block of the union is gathered from HBM once and serves both
+// query blocks, so the gather traffic drops to the union's share.  Waves 0-1
+// own the pair's first query block and waves 2-3 its second; wave qh of a
+// half computes queries 32*qh .. +31 against all 64 KV rows of every block
+// it holds (two 32x32 score tiles, each reused over a 128-deep
+// contraction), so a query's whole row of a block lives in one wave and the
+// online softmax needs no merge.  A half skips the union blocks its own list
+// does not hold.  Each SIMD runs one wave of each of the CU's two
+// workgroups: they wait at different barriers, so one's MFMA work can run
+// beside the other's softmax.  K and V stay row-major in LDS (V^T fragments
+// come from ds_read_b64_tr_b16), copied straight from HBM into two slots
+// (buffer loads with the LDS modifier, no staging registers): the next
+// union entry lands in one slot while the current one is read from the
+// other.
 template <int D>
-__global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ kv_idx,
@@ -47,31 +47,29 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
     uint16_t* __restrict__ o, float* __restrict__ lse) {
   using namespace tiles;
   using TL = Tile<D>;
-  using SH = Share<D, 512>;
+  using SH = Share<D, 256>;
   constexpr int KS = D / 16;     // k-steps of S^T = K Q^T
   constexpr int DT = D / 32;     // 32-row d tiles of O^T
   constexpr int KP = SH::kPerThread;
   const int Nb = N / 64;
-  // LDS: two sets of two K/V slots (slot u of a set: K, then V of one
-  // block, at u * 2 tiles), as two separate arrays so that the compiler sees
-  // that reads of one set never wait for copies into the other; the union
-  // list in dynamic LDS.  The union's membership bitmaps live in set 0 while
-  // the list is built (before any tile is copied).
-  __shared__ __align__(16) unsigned char set0[4 * TL::kBytes];
-  __shared__ __align__(16) unsigned char set1[4 * TL::kBytes];
+  // LDS: two K/V slots (K, then V of one block) as separate arrays, so the
+  // compiler sees that reads of one slot never wait for copies into the
+  // other; the union list in dynamic LDS.  The union's membership bitmaps
+  // live in slot 0 while the list is built (before any tile is copied).
+  __shared__ __align__(16) unsigned char slot0[2 * TL::kBytes];
+  __shared__ __align__(16) unsigned char slot1[2 * TL::kBytes];
   extern __shared__ __align__(16) unsigned char dyn[];
   uint16_t* ulist = reinterpret_cast<uint16_t*>(dyn);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(set0);
-  __shared__ float sm_m[2][2][32], sm_l[2][2][32];
-  __shared__ int s_cnt[8];
+  uint32_t* bits = reinterpret_cast<uint32_t*>(slot0);
+  __shared__ int s_cnt[4];
 
   long long bh;
   int pr;
   if (!xcd_item((Nb + 1) / 2, total, bh, pr)) return;
   const int b = (int)(bh / Hh);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int half = __builtin_amdgcn_readfirstlane(wave >> 2);
-  const int qh = wave & 1, kh = (wave >> 1) & 1;
+  const int half = __builtin_amdgcn_readfirstlane(wave >> 1);
+  const int qh = wave & 1;
   const int c = lane & 31, hf = lane >> 5, j16 = lane & 15, grp = lane >> 4;
   const long long head = bh * N;
   const int32_t* pb = perm + (long long)b * N;
@@ -85,7 +83,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
   const int32_t* lst0 = kv_idx + row0 * (long long)capacity;
   const int32_t* lst1 = kv_idx + (bh * Nb + i1) * (long long)capacity;
 
-  const int ucnt = pair_union(lst0, cnt0, lst1, cnt1, Nb, bits, ulist, s_cnt, tid);
+  const int ucnt = pair_union<256>(lst0, cnt0, lst1, cnt1, Nb, bits, ulist, s_cnt, tid);
 
   // a missing second block borrows the first one's rows (never written)
   const int iq = half == 1 ? i1 : i0;
@@ -101,161 +99,116 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
   f32x16 oacc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) oacc[t] = f32x16{};
-  const int krow = 32 * kh + slot_of(c);   // K row feeding this lane's M-row
+  // K rows feeding this lane's M-rows of the two score tiles
+  const int krow0 = slot_of(c), krow1 = 32 + slot_of(c);
 
   const __amdgpu_buffer_rsrc_t rk = head_rsrc<D>(k, head, N);
   const __amdgpu_buffer_rsrc_t rv = head_rsrc<D>(v, head, N);
-  uint32_t offA[KP], offB[KP];
+  uint32_t offn[KP];
   // an empty union leaves ulist[0] = block 0 (pair_union), a safe id for
   // the prologue's loads; the loop then runs no step
   const int last = max(ucnt - 1, 0);
   auto uid = [&](int t) __attribute__((always_inline)) -> int {
     return (int)(ulist[min(t, last)] & 0x1fffu);
   };
-  auto slot = [&](int set, int u) __attribute__((always_inline)) {
-    return (set ? set1 : set0) + u * 2 * TL::kBytes;
-  };
-  // prologue: entries 0, 1 copied into set 0, offsets of entries 2, 3.
-  // Past the end of the list the last block is re-fetched, so the loop body
-  // has no branches around the loads and the wait counters stay exact.
+  // prologue: entry 0 copied into slot 0, offsets of entry 1.  Past the end
+  // of the list the last block is re-fetched, so the loop body has no
+  // branches around the loads and the wait counters stay exact.
   {
     int rows[KP];
-    stage_rows<D, 512>(rows, pb, uid(0), tid);
-    dma_offsets<D, 512>(offA, rows, tid);
-    stage_rows<D, 512>(rows, pb, uid(1), tid);
-    dma_offsets<D, 512>(offB, rows, tid);
-    stage_dma<D, 512>(slot(0, 0), rk, offA, tid);
-    stage_dma<D, 512>(slot(0, 0) + TL::kBytes, rv, offA, tid);
-    stage_dma<D, 512>(slot(0, 1), rk, offB, tid);
-    stage_dma<D, 512>(slot(0, 1) + TL::kBytes, rv, offB, tid);
-    stage_rows<D, 512>(rows, pb, uid(2), tid);
-    dma_offsets<D, 512>(offA, rows, tid);
-    stage_rows<D, 512>(rows, pb, uid(3), tid);
-    dma_offsets<D, 512>(offB, rows, tid);
+    stage_rows<D, 256>(rows, pb, uid(0), tid);
+    dma_offsets<D, 256>(offn, rows, tid);
+    stage_dma<D, 256>(slot0, rk, offn, tid);
+    stage_dma<D, 256>(slot0 + TL::kBytes, rv, offn, tid);
+    stage_rows<D, 256>(rows, pb, uid(1), tid);
+    dma_offsets<D, 256>(offn, rows, tid);
   }
 
-  // S^T (32 kv x 32 q) = K_half Q_half^T of the block in slot sk
-  auto scores = [&](const unsigned char* sk) __attribute__((always_inline)) {
-    f32x16 s = f32x16{};
+  // one block: S^T (64 kv x 32 q, two tiles), online softmax over the 64
+  // keys, O^T (d x 32 q) += V^T P^T
+  auto compute_block = [&](const unsigned char* sk) __attribute__((always_inline)) {
+    const unsigned char* sv = sk + TL::kBytes;
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      s = mfma32(lds_row8<D>(sk, krow, 2 * ks + hf), qreg[ks], s);
-    return s;
-  };
-  // Online softmax in the log2 domain (scale > 0, so the max of the raw
-  // scores is the max of the scaled ones).  The exponent reference only
-  // moves when a block's max exceeds it by more than 8: until then the
-  // probabilities stay <= 2^8 (exact range in fp32 and bf16) and the
-  // accumulator needs no rescale.  Returns the new reference.
-  auto block_max = [&](const f32x16& s, float m_ref) __attribute__((always_inline)) {
-    float mx = s[0];
+    for (int ks = 0; ks < KS; ++ks) {
+      s0 = mfma32(lds_row8<D>(sk, krow0, 2 * ks + hf), qreg[ks], s0);
+      s1 = mfma32(lds_row8<D>(sk, krow1, 2 * ks + hf), qreg[ks], s1);
+    }
+    // online softmax in the log2 domain (scale > 0, so the max of the raw
+    // scores is the max of the scaled ones).  The exponent reference only
+    // moves when a block's max exceeds it by more than 8: until then the
+    // probabilities stay <= 2^8 (exact range in fp32 and bf16) and the
+    // accumulator needs no rescale.
+    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
     mx = xor32_max(mx) * scale_log2;
-    return mx > m_ref + 8.f ? mx : m_ref;
-  };
-  // probabilities 2^(s scale - m) in place; returns their sum over the lane
-  // pair (one query's 32 keys)
-  auto probs = [&](f32x16& s, float m) __attribute__((always_inline)) {
+    const float m_new = mx > m_run + 8.f ? mx : m_run;
+    const float alpha = exp2_fast(m_run - m_new);
     float rs = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s[r] = exp2_fast(fmaf(s[r], scale_log2, -m));
-      rs += s[r];
+      s0[r] = exp2_fast(fmaf(s0[r], scale_log2, -m_new));
+      s1[r] = exp2_fast(fmaf(s1[r], scale_log2, -m_new));
+      rs += s0[r] + s1[r];
     }
-    return xor32_sum(rs);
-  };
-  // O^T (d x 32 q) += V_half^T P^T of the block whose V tile is sv
-  auto pv = [&](const unsigned char* sv, const f32x16& p) __attribute__((always_inline)) {
-    const bf16x8 p0 = pack8(p, 0), p1 = pack8(p, 1);
+    rs = xor32_sum(rs);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {      // the reference moved for some query
+#pragma unroll
+      for (int t2 = 0; t2 < DT; ++t2) oacc[t2] *= alpha;
+    }
+    const bf16x8 p00 = pack8(s0, 0), p01 = pack8(s0, 1);
+    const bf16x8 p10 = pack8(s1, 0), p11 = pack8(s1, 1);
 #pragma unroll
     for (int mt = 0; mt < DT; ++mt) {
       const int d0 = 32 * mt + 16 * (grp & 1);
-      const int r0 = 32 * kh + 8 * (grp >> 1);
-      oacc[mt] = mfma32(lds_tr8<D>(sv, r0, d0, j16), p0, oacc[mt]);
-      oacc[mt] = mfma32(lds_tr8<D>(sv, r0 + 16, d0, j16), p1, oacc[mt]);
+      const int r0 = 8 * (grp >> 1);
+      oacc[mt] = mfma32(lds_tr8<D>(sv, r0, d0, j16), p00, oacc[mt]);
+      oacc[mt] = mfma32(lds_tr8<D>(sv, r0 + 16, d0, j16), p01, oacc[mt]);
+      oacc[mt] = mfma32(lds_tr8<D>(sv, r0 + 32, d0, j16), p10, oacc[mt]);
+      oacc[mt] = mfma32(lds_tr8<D>(sv, r0 + 48, d0, j16), p11, oacc[mt]);
     }
   };
-  auto rescale = [&](float f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int t2 = 0; t2 < DT; ++t2) oacc[t2] *= f;
-  };
 
-  auto compute_one = [&](const unsigned char* sk) __attribute__((always_inline)) {
-    f32x16 s = scores(sk);
-    const float m_new = block_max(s, m_run);
-    const float alpha = exp2_fast(m_run - m_new);
-    const float rs = probs(s, m_new);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) rescale(alpha);   // the reference moved for some query
-    pv(sk + TL::kBytes, s);
-  };
-// One step over union entries 2 ss, 2 ss + 1 (in set SET_): once every
-// wave's copies into that set have landed, start copying entries 2 ss + 2,
-// + 3 into the other set, load the rows of entries 2 ss + 4, + 5 (issued
-// first: the wait for them then leaves the copies in flight), compute this
-// half's blocks of the step, then turn the rows into offsets.
-#define PRISM_FWD_STEP(SS_, SET_)                                           \
+// One union entry t (in slot SLOT_): once every wave's copies into that
+// slot have landed, start copying entry t+1 into the other slot, load the
+// rows of entry t+2 (issued first: the wait for them then leaves the copy
+// in flight), compute entry t if this half's list holds it, then turn the
+// rows into offsets.
+#define PRISM_FWD_STEP(T_, SLOT_, OTHER_)                                   \
   {                                                                         \
-    const int e0i = 2 * (SS_);                                              \
+    const int tt = (T_);                                                    \
     wait_loads();                                                           \
     __syncthreads();                                                        \
-    int rowsA[KP], rowsB[KP];                                               \
-    stage_rows<D, 512>(rowsA, pb, uid(e0i + 4), tid);                       \
-    stage_rows<D, 512>(rowsB, pb, uid(e0i + 5), tid);                       \
+    int rows_n[KP];                                                         \
+    stage_rows<D, 256>(rows_n, pb, uid(tt + 2), tid);                       \
     pin_order();                                                            \
-    stage_dma<D, 512>(slot(1 - (SET_), 0), rk, offA, tid);                  \
-    stage_dma<D, 512>(slot(1 - (SET_), 0) + TL::kBytes, rv, offA, tid);     \
-    stage_dma<D, 512>(slot(1 - (SET_), 1), rk, offB, tid);                  \
-    stage_dma<D, 512>(slot(1 - (SET_), 1) + TL::kBytes, rv, offB, tid);     \
+    stage_dma<D, 256>(OTHER_, rk, offn, tid);                               \
+    stage_dma<D, 256>(OTHER_ + TL::kBytes, rv, offn, tid);                  \
     pin_order();                                                            \
-    const uint32_t ea = __builtin_amdgcn_readfirstlane((uint32_t)ulist[e0i]); \
-    const uint32_t eb = e0i + 1 < ucnt                                      \
-        ? __builtin_amdgcn_readfirstlane((uint32_t)ulist[e0i + 1]) : 0u;    \
-    const bool ha = (ea & mflag) != 0, hb = (eb & mflag) != 0;             \
-    if (ha) compute_one(slot((SET_), 0));                                   \
-    if (hb) compute_one(slot((SET_), 1));                                   \
-    dma_offsets<D, 512>(offA, rowsA, tid);                                  \
-    dma_offsets<D, 512>(offB, rowsB, tid);                                  \
+    const uint32_t e = __builtin_amdgcn_readfirstlane((uint32_t)ulist[tt]); \
+    if (e & mflag) compute_block(SLOT_);                                    \
+    dma_offsets<D, 256>(offn, rows_n, tid);                                 \
   }
 
-  // set 0 at even steps, set 1 at odd ones
-  const int nss = (ucnt + 1) / 2;
-  int ss = 0;
-  for (; ss + 1 < nss; ss += 2) {
-    PRISM_FWD_STEP(ss, 0)
-    PRISM_FWD_STEP(ss + 1, 1)
+  // slot 0 at even entries, slot 1 at odd ones
+  int t = 0;
+  for (; t + 1 < ucnt; t += 2) {
+    PRISM_FWD_STEP(t, slot0, slot1)
+    PRISM_FWD_STEP(t + 1, slot1, slot0)
   }
-  if (ss < nss) PRISM_FWD_STEP(ss, 0)
+  if (t < ucnt) PRISM_FWD_STEP(t, slot0, slot1)
 #undef PRISM_FWD_STEP
-
-  // merge the two KV halves of each query half: waves kh = 1 hand over
-  // (m, l, O) through LDS (2 waves x 64 lanes x D/2 floats = 2 * kBytes per
-  // query block).  The copies issued past the end of the list land first.
+  // the copies issued past the end of the list land before the workgroup
+  // ends (nothing reads them)
   wait_loads();
-  __syncthreads();
-  float* xo = reinterpret_cast<float*>(set0 + half * 2 * TL::kBytes);
-  if (kh == 1) {
-    if (hf == 0) {
-      sm_m[half][qh][c] = m_run;
-      sm_l[half][qh][c] = l_run;
-    }
-#pragma unroll
-    for (int mt = 0; mt < DT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        xo[((qh * 64 + lane) * DT + mt) * 16 + r] = oacc[mt][r];
-  }
-  __syncthreads();
-  if (kh == 0 && (half == 0 || has_second)) {
-    const float m2 = sm_m[half][qh][c], l2 = sm_l[half][qh][c];
-    float m = fmaxf(m_run, m2);
+
+  if (half == 0 || has_second) {
+    float m = m_run, l = l_run;
     // m = -inf: the query block's list is empty (no key at all)
     const bool none = m == -INFINITY;
-    const float a1 = none ? 0.f : exp2_fast(m_run - m);
-    const float a2 = none ? 0.f : exp2_fast(m2 - m);
-    float l = l_run * a1 + l2 * a2;
     // optional stand-in of the blocks this query block did not keep: weight
     // exp(drop_lse) (natural log) with value drop_v, one more term of the
     // same softmax
@@ -281,8 +234,7 @@ __global__ __launch_bounds__(512, 2) void attn_fwd_bf16(
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int r = 4 * a + bb;
-          const float x = oacc[mt][r] * a1 +
-                          xo[((qh * 64 + lane) * DT + mt) * 16 + r] * a2;
+          const float x = oacc[mt][r];
           vals[bb] = dvr ? (x * b1 + b2 * dvr[32 * mt + 8 * a + 4 * hf + bb]) * inv_l
                          : x * inv_l;
         }
@@ -399,13 +351,13 @@ prism_status launch_attn_fwd(const void* q, const void* k, const void* v,
     if (d == 128) {
       // the 16-bit union list (the tiles are static LDS)
       const size_t dyn = 2 * (size_t)Nb;
-      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<128>, g1, dim3(512), dyn, stream,
+      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<128>, g1, dim3(256), dyn, stream,
                    (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                    perm, counts, kv_idx, capacity, pairs, Hh, N, total, sl2,
                    drop_lse, drop_v, (uint16_t*)o, lse);
     } else {
       const size_t dyn = 2 * (size_t)Nb;
-      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<64>, g1, dim3(512), dyn, stream,
+      PRISM_LAUNCH("attn_fwd_bf16", attn_fwd_bf16<64>, g1, dim3(256), dyn, stream,
                    (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                    perm, counts, kv_idx, capacity, pairs, Hh, N, total, sl2,
                    drop_lse, drop_v, (uint16_t*)o, lse);

@@ -331,13 +331,15 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int s) {
   return as_bf16x8(u);
 }
 
-// Ascending union of two blocks' KV lists, built by a 512-thread workgroup.
+// Ascending union of two blocks' KV lists, built by a workgroup of NT
+// threads (NT = 256 or 512; thread w owns bitmap word w of the union).
 // Each 16-bit entry is id | (in list 0) << 13 | (in list 1) << 14 (ids
 // fit 13 bits: Nb <= 8192).  bits holds 2 * ceil(Nb / 32) words and ulist
 // Nb entries (LDS); s_cnt 8 ints.  Counts are clamped to [0, Nb], ids outside [0, Nb) are
 // skipped and duplicates merge, so any list gives a valid union.  Returns
 // the union size; when it is 0, ulist[0] holds block 0 with no membership
 // bits (a safe id for the gather prologue).  Ends with a barrier.
+template <int NT = 512>
 __device__ __forceinline__ int pair_union(const int32_t* __restrict__ lst0,
                                           int cnt0,
                                           const int32_t* __restrict__ lst1,
@@ -345,21 +347,21 @@ __device__ __forceinline__ int pair_union(const int32_t* __restrict__ lst0,
                                           uint16_t* ulist, int* s_cnt, int tid) {
   const int words = (Nb + 31) / 32;
   const int wave = tid >> 6, lane = tid & 63;
-  for (int w = tid; w < 2 * words; w += 512) bits[w] = 0u;
+  for (int w = tid; w < 2 * words; w += NT) bits[w] = 0u;
   __syncthreads();
   cnt0 = min(max(cnt0, 0), Nb);
   cnt1 = min(max(cnt1, 0), Nb);
-  for (int t = tid; t < cnt0; t += 512) {
+  for (int t = tid; t < cnt0; t += NT) {
     const int j = lst0[t];
     if ((unsigned)j < (unsigned)Nb) atomicOr(&bits[j >> 5], 1u << (j & 31));
   }
-  for (int t = tid; t < cnt1; t += 512) {
+  for (int t = tid; t < cnt1; t += NT) {
     const int j = lst1[t];
     if ((unsigned)j < (unsigned)Nb)
       atomicOr(&bits[words + (j >> 5)], 1u << (j & 31));
   }
   __syncthreads();
-  // thread w owns bitmap word w (words <= 256)
+  // thread w owns bitmap word w (words <= 256 <= NT)
   const uint32_t wa = tid < words ? bits[tid] : 0u;
   const uint32_t wb = tid < words ? bits[words + tid] : 0u;
   uint32_t wu = wa | wb;
@@ -374,7 +376,7 @@ __device__ __forceinline__ int pair_union(const int32_t* __restrict__ lst0,
   __syncthreads();
   int pos = incl - n, ucnt = 0;
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const int x = s_cnt[w];
     pos += w < wave ? x : 0;
     ucnt += x;
