@@ -70,8 +70,9 @@ __global__ __launch_bounds__(256) void bwd_delta(const E* __restrict__ o,
 // Waves 0-3 own the pair's first KV block and waves 4-7 its second; within
 // a half, wave (kh, qh) computes KV rows 32*kh .. +31 (K, V of the block resident in LDS, B
 // operands) against query rows 32*qh .. +31.  A half skips the query blocks
-// that did not select its KV block.  Q and dO go through two LDS buffers,
-// staged one block ahead in registers; Q^T / dO^T fragments come from
+// that did not select its KV block.  Q and dO are copied straight from HBM
+// into two LDS slots (buffer loads with the LDS modifier, no staging
+// registers), one union entry ahead; Q^T / dO^T fragments come from
 // ds_read_b64_tr_b16.  The two qh waves of a KV half sum their partial dK /
 // dV at the end.
 template <int D>
@@ -86,11 +87,16 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
   using TL = Tile<D>;
   using SH = Share<D, 512>;
   constexpr int KS = D / 16, DT = D / 32;
+  constexpr int KP = SH::kPerThread;
+  // Q, dO of one union entry per slot (separate arrays, so reads of one
+  // slot never wait for copies into the other), K, V of both KV blocks, the
+  // lse / D rows of the two slots; the union list in dynamic LDS
+  __shared__ __align__(16) unsigned char qo0[2 * TL::kBytes];
+  __shared__ __align__(16) unsigned char qo1[2 * TL::kBytes];
+  __shared__ __align__(16) unsigned char skv[4 * TL::kBytes];   // half h: K, V
+  __shared__ __align__(16) float sx[256];                        // slot u: lse, D
   extern __shared__ __align__(16) unsigned char dyn[];
-  unsigned char* sqo = dyn;                         // buffer u: Q, dO tiles
-  unsigned char* skv = dyn + 4 * TL::kBytes;        // half h: K, V tiles
-  float* sx = reinterpret_cast<float*>(dyn + 8 * TL::kBytes);  // buffer u: lse, D
-  uint16_t* ulist = reinterpret_cast<uint16_t*>(sx + 256);
+  uint16_t* ulist = reinterpret_cast<uint16_t*>(dyn);
   __shared__ int s_cnt[8];
 
   const int Nb = N / 64;
@@ -189,16 +195,16 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
   RowAddr ra_q = row_addr<D>(arow, hf), ra_k = row_addr<D>(brow, hf);
   TrAddr ta = tr_addr<D>(32 * qh, lane);
 
-  // Q / dO tiles and one lse (tid < 64) or D (64 <= tid < 128) per thread
-  // are staged one block ahead in registers and published into two LDS
-  // buffers; lse is scaled to log2 units when it is published
+  // Q / dO tiles are copied into the two slots one union entry ahead; one
+  // lse (tid < 64) or D (64 <= tid < 128) value per thread is staged one
+  // entry ahead in a register (its row two entries ahead) and published
+  // into the slot's lse / D row, lse scaled to log2 units
   const float* xsrc = (tid < 64 ? lse : delta) + head;
   const float xscale = tid < 64 ? kLog2e : 1.f;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc<D>(q, head, N);
   const __amdgpu_buffer_rsrc_t ro = head_rsrc<D>(d_o, head, N);
-  Stage<D, 512> qS, oS;
   float xS = 0.f;
-  uint32_t offs_n[SH::kPerThread];
+  uint32_t offn[KP];
   int xrow_n = 0;
   const int last = ucnt - 1;
   auto uid = [&](int t) __attribute__((always_inline)) -> int {
@@ -207,28 +213,23 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
   auto xload = [&](int blk) __attribute__((always_inline)) -> int {
     return pb[64 * blk + (tid & 63)];
   };
-  int j_n = 0;
   {
-    // entry 0 published to buffer 0, entry 1 staged, offsets and lse / D
-    // row of entry 2, id of entry 3
-    uint32_t o0[SH::kPerThread];
+    // entry 0 copied into slot 0 with its lse / D row, entry 1's offsets
+    // and lse / D value, entry 2's lse / D row.  Past the end of the list
+    // the last block is re-fetched.
+    int rows[KP];
     int u = uid(0);
-    stage_offsets<D, 512>(o0, pb, u, tid);
-    stage_load<D, 512>(qS, rq, o0);
-    stage_load<D, 512>(oS, ro, o0);
-    xS = xsrc[xload(u)];
-    stage_store<D, 512>(qS, sqo, tid);
-    stage_store<D, 512>(oS, sqo + TL::kBytes, tid);
-    if (tid < 128) sx[tid] = xS * xscale;
+    stage_rows<D, 512>(rows, pb, u, tid);
+    dma_offsets<D, 512>(offn, rows, tid);
+    stage_dma<D, 512>(qo0, rq, offn, tid);
+    stage_dma<D, 512>(qo0 + TL::kBytes, ro, offn, tid);
+    const float x0 = xsrc[xload(u)];
+    if (tid < 128) sx[tid] = x0 * xscale;
     u = uid(1);
-    stage_offsets<D, 512>(o0, pb, u, tid);
-    stage_load<D, 512>(qS, rq, o0);
-    stage_load<D, 512>(oS, ro, o0);
+    stage_rows<D, 512>(rows, pb, u, tid);
+    dma_offsets<D, 512>(offn, rows, tid);
     xS = xsrc[xload(u)];
-    u = uid(2);
-    stage_offsets<D, 512>(offs_n, pb, u, tid);
-    xrow_n = xload(u);
-    j_n = uid(3);
+    xrow_n = xload(uid(2));
   }
 
   auto compute_block = [&](const unsigned char* sq, const float* s_lse)
@@ -267,49 +268,51 @@ __global__ __launch_bounds__(512, 2) void dkdv_bf16(
     }
   };
 
-// One union entry t (in buffer t % 2): publish the staged entry t+1 into the
-// other buffer, load the rows and lse / D of later entries, refill the stage
-// with entry t+2, compute entry t if it selected this half's KV block.
-#define PRISM_DKDV_STEP(T_, BUF_)                                           \
+// One union entry t (in slot SLOT_, lse / D row XB_): once every wave's
+// copies into that slot have landed, publish entry t+1's lse / D into the
+// other row, load entry t+2's lse / D and rows and entry t+3's lse / D row
+// (issued first: the waits for them leave the copies in flight), start
+// copying entry t+1 into the other slot, compute entry t if it selected
+// this half's KV block, then turn the rows into offsets.
+#define PRISM_DKDV_STEP(T_, SLOT_, OTHER_, XB_)                             \
   {                                                                         \
     const int tt = (T_);                                                    \
+    wait_loads();                                                           \
     __syncthreads();                                                        \
-    stage_store<D, 512>(qS, sqo + (1 - (BUF_)) * 2 * TL::kBytes, tid);      \
-    stage_store<D, 512>(oS, sqo + (1 - (BUF_)) * 2 * TL::kBytes +           \
-                                TL::kBytes, tid);                           \
-    if (tid < 128) sx[(1 - (BUF_)) * 128 + tid] = xS * xscale;              \
+    if (tid < 128) sx[(1 - (XB_)) * 128 + tid] = xS * xscale;               \
     const float x_n = xsrc[xrow_n];                                         \
-    int rows_n[SH::kPerThread];                                             \
-    stage_rows<D, 512>(rows_n, pb, j_n, tid);                               \
-    const int xrow_nn = xload(j_n);                                         \
+    int rows_n[KP];                                                         \
+    stage_rows<D, 512>(rows_n, pb, uid(tt + 2), tid);                       \
+    const int xrow_nn = xload(uid(tt + 3));                                 \
     pin_order();                                                            \
-    stage_load<D, 512>(qS, rq, offs_n);                                     \
-    stage_load<D, 512>(oS, ro, offs_n);                                     \
+    stage_dma<D, 512>(OTHER_, rq, offn, tid);                               \
+    stage_dma<D, 512>(OTHER_ + TL::kBytes, ro, offn, tid);                  \
     pin_order();                                                            \
-    xS = x_n;                                                               \
-    j_n = uid(tt + 4);                                                      \
     const uint32_t e = __builtin_amdgcn_readfirstlane((uint32_t)ulist[tt]); \
     opaque(ra_q);                                                           \
     opaque(ra_k);                                                           \
     opaque(ta);                                                             \
-    if (e & mflag)                                                          \
-      compute_block(sqo + (BUF_) * 2 * TL::kBytes, sx + (BUF_) * 128);      \
-    rows_to_offsets<D, 512>(offs_n, rows_n, tid);                           \
+    if (e & mflag) compute_block(SLOT_, sx + (XB_) * 128);                  \
+    dma_offsets<D, 512>(offn, rows_n, tid);                                 \
+    xS = x_n;                                                               \
     xrow_n = xrow_nn;                                                       \
   }
 
   int t = 0;
   for (; t + 1 < ucnt; t += 2) {
-    PRISM_DKDV_STEP(t, 0)
-    PRISM_DKDV_STEP(t + 1, 1)
+    PRISM_DKDV_STEP(t, qo0, qo1, 0)
+    PRISM_DKDV_STEP(t + 1, qo1, qo0, 1)
   }
-  if (t < ucnt) PRISM_DKDV_STEP(t, 0)
+  if (t < ucnt) PRISM_DKDV_STEP(t, qo0, qo1, 0)
 #undef PRISM_DKDV_STEP
+  // the copies issued past the end of the list land before the slots are
+  // reused below
+  wait_loads();
 
-  // sum the two qh partials of each KV half: qh = 1 hands over through LDS,
-  // one tensor at a time (2 waves x 64 lanes x D/2 floats = 2 * kBytes per
-  // half)
-  float* xch = reinterpret_cast<float*>(sqo + half * 2 * TL::kBytes);
+  // sum the two qh partials of each KV half: qh = 1 hands over through LDS
+  // (half h uses slot h), one tensor at a time (2 waves x 64 lanes x D/2
+  // floats = 2 * kBytes per half)
+  float* xch = reinterpret_cast<float*>(half ? qo1 : qo0);
   float* dvr = dv + (head + kvrow) * D;
   float* dkr = dk + (head + kvrow) * D;
   const bool write = half == 0 || has_second;
@@ -659,8 +662,8 @@ prism_status run_bwd(const void* q, const void* k, const void* v,
       return st;
     const long long heads = (long long)B * Hh;
     const dim3 gp(tiles::xcd_grid((Nb + 1) / 2, heads));
-    const size_t dyn = 8 * tiles::Tile<D>::kBytes + 256 * sizeof(float) +
-                       (size_t)Nb * sizeof(uint16_t);
+    // the 16-bit union list (tiles and lse / D rows are static LDS)
+    const size_t dyn = (size_t)Nb * sizeof(uint16_t);
     PRISM_LAUNCH("dkdv_bf16", dkdv_bf16<D>, gp, dim3(512), dyn, stream,
                  (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                  (const uint16_t*)d_o, lse, delta, perm, bits, words, kpairs, Hh, N,
