@@ -8,7 +8,8 @@
 //
 // bf16 path (gfx950 MFMA v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //   every wave computes S^T = K Q^T (kv x q), so a lane holds 16 scores of
-//   one query and the row statistics need one cross-lane step; the K rows
+//   one query per 32-key tile and the row statistics need one cross-lane
+//   step; the K rows
 //   feeding the M-rows are ordered (tiles::slot_of) so that the lane's
 //   probabilities are already the B operand of O^T += V^T P^T -- P never
 //   goes through LDS.
@@ -21,7 +22,8 @@ namespace {
 
 // One workgroup of 4 waves per pair of query blocks (pairs[p]: neighbours
 // in the permuted order whose lists overlap most, see pairing.hip), two
-// workgroups per CU.  The two lists are merged into one ascending union in
+// workgroups per CU (64 KiB of tiles + 2 Nb bytes of list each: two fit for
+// Nb below 8184).  The two lists are merged into one ascending union in
 // LDS; each K/V block of the union is gathered from HBM once and serves both
 // query blocks, so the gather traffic drops to the union's share.  Waves 0-1
 // own the pair's first query block and waves 2-3 its second; wave qh of a
