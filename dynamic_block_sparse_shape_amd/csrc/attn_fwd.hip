@@ -141,9 +141,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16(
     // moves when a block's max exceeds it by more than 8: until then the
     // probabilities stay <= 2^8 (exact range in fp32 and bf16) and the
     // accumulator needs no rescale.
-    float mx = fmaxf(s0[0], s1[0]);
+    float mx = fmax_prop(s0[0], s1[0]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    for (int r = 1; r < 16; ++r) mx = fmax_prop(mx, fmax_prop(s0[r], s1[r]));
     mx = xor32_max(mx) * scale_log2;
     const float m_new = mx > m_run + 8.f ? mx : m_run;
     const float alpha = exp2_fast(m_run - m_new);

@@ -303,12 +303,21 @@ __device__ __forceinline__ uint32_t cvt2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
+// Maximum that propagates NaN (IEEE 754-2019 maximum, v_maximum3_f32 on
+// gfx950).  fmaxf drops a NaN operand, which in IEEE mode makes the compiler
+// quiet every input first (one extra v_max_f32 x, x, x per score); for the
+// finite scores of a row both give the same maximum, and a NaN score makes
+// the row NaN either way (its exponential is NaN).
+__device__ __forceinline__ float fmax_prop(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+
 // Combine a value with the one held by lane l ^ 32: v_permlane32_swap
 // (gfx950) hands every lane its partner's value without touching LDS.
 __device__ __forceinline__ float xor32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
                                                   __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_prop(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float xor32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),

@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256, 2) void bridge_attn(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       if (64 * t + kof[r] >= Na) s[r] = -INFINITY;
-      mx = fmaxf(mx, s[r]);
+      mx = fmax_prop(mx, s[r]);
     }
     mx = xor32_max(mx) * scale_log2;
     const float m_new = mx > m_run + 8.f ? mx : m_run;
