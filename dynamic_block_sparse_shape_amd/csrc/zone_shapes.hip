@@ -127,18 +127,41 @@ __global__ __launch_bounds__(kThreads) void zone_feat_dev(
   constexpr int kPieces = kRowBytes / 16;
   constexpr int kIter = kMaxZoneTokens * kPieces / kThreads;
   const unsigned char* fb = feat + (long long)b * N * rowB + (long long)c0 * sizeof(E);
+  // thread tid covers piece tid % kPieces of tokens tid / kPieces + kStep * it.
+  // The token's (h, w) place in the zone and its byte offset in the feature
+  // map are computed once and then advanced by kStep tokens in the zone's
+  // mixed radix (Lt, Lh, Lw), with carries: no division or multiplication
+  // per load.
+  constexpr int kStep = kThreads / kPieces;
+  const int piece = threadIdx.x % kPieces;
+  const int plane = zb.Lh * zb.Lw;
+  int tok = threadIdx.x / kPieces;
+  const int lt0 = tok / plane;
+  int lh = (tok - lt0 * plane) / zb.Lw;
+  int lw = tok - lt0 * plane - lh * zb.Lw;
+  const int dt = kStep / plane;
+  const int dh = (kStep - dt * plane) / zb.Lw;
+  const int dw = kStep - dt * plane - dh * zb.Lw;
+  const long long RW = rowB, RH = (long long)g.W * rowB, RT = (long long)g.H * RH;
+  const long long step = dw * RW + dh * RH + dt * RT;   // kStep tokens, no carry
+  const long long carry_w = RH - zb.Lw * RW;            // w wraps: next h
+  const long long carry_h = RT - zb.Lh * RH;            // h wraps: next t
+  long long gofs = (((long long)(zb.t0 + lt0) * g.H + (zb.h0 + lh)) * g.W + zb.w0 + lw) * rowB +
+                   piece * 16;
   uint4 v[kIter];
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
-    const int i = threadIdx.x + it * kThreads;
-    const int tok = i / kPieces, piece = i % kPieces;
     v[it] = make_uint4(0, 0, 0, 0);
-    if (tok < nt && piece * 16 < valid_bytes) {
-      const int lw = tok % zb.Lw, lh = (tok / zb.Lw) % zb.Lh, lt = tok / (zb.Lw * zb.Lh);
-      const long long gtok =
-          ((long long)(zb.t0 + lt) * g.H + (zb.h0 + lh)) * g.W + zb.w0 + lw;
-      v[it] = *reinterpret_cast<const uint4*>(fb + gtok * rowB + piece * 16);
-    }
+    if (tok < nt && piece * 16 < valid_bytes)
+      v[it] = *reinterpret_cast<const uint4*>(fb + gofs);
+    tok += kStep;
+    lw += dw;
+    const bool cw = lw >= zb.Lw;
+    lw -= cw ? zb.Lw : 0;
+    lh += dh + (cw ? 1 : 0);
+    const bool ch = lh >= zb.Lh;
+    lh -= ch ? zb.Lh : 0;
+    gofs += step + (cw ? carry_w : 0ll) + (ch ? carry_h : 0ll);
   }
 #pragma unroll
   for (int it = 0; it < kIter; ++it) {
